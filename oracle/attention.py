@@ -1,0 +1,158 @@
+"""Causal softmax attention of every query over exactly its own pages, in fp64.
+
+The union method is exact: masked query-page slots are excluded and every
+selected edge is retained (PageWeaver Fig. 2 caption), each query keeps its
+original support and owns its complete output row (abstract).  So the result
+is the plain definition below; grouping only changes how it is reached.
+
+Notation (readings where the pages are silent are listed in the design notes):
+query i sits at position p_i = q_pos[i]; query head h reads KV head
+g = h // G; token t lies on page t // ps; the allowed keys of (i, g) are
+
+    J(i, g) = { t : t // ps in S(i, g),  t <= p_i,  t < kv_len }
+
+and, with s_t = sigma * <Q[i, h], K[g, t]>,
+
+    O[i, h] = sum_{t in J} exp(s_t - m) V[g, t] / sum_{t in J} exp(s_t - m),
+    lse[i, h] = m + log sum_{t in J} exp(s_t - m),   m = max_{t in J} s_t,
+
+with O = 0 and lse = -inf when J is empty.  K and V are the decoded cache
+values (bf16 exact, or e4m3fn code times the page scale, exact in fp64).
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+from .numerics import bf16_bits_to_f64, decode_kv
+
+
+def _softmax_pv(s: np.ndarray, v: np.ndarray):
+    """s [R, n] scores, v [n, d] -> (O [R, d], lse [R]); n == 0 gives zeros / -inf."""
+    R, n = s.shape
+    if n == 0:
+        return np.zeros((R, v.shape[1])), np.full(R, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    return (e @ v) / l, (m + np.log(l))[:, 0]
+
+
+def route_a(q_bits, k_data, v_data, k_scale, v_scale, kv_dtype: str,
+            S: List[List[frozenset]], q_pos, kv_len: int, ps: int, sm_scale: float,
+            queries: Optional[Sequence[int]] = None):
+    """Per-query gather of the selected pages: the definition.
+
+    q_bits uint16 [nq, hq, d]; k_data/v_data [hkv, n_pages, ps, d]; S[g][i] sets.
+    Returns O fp64 [n_sel, hq, d] and lse fp64 [n_sel, hq] for ``queries``
+    (default: all) in the order given.
+    """
+    nq, hq, d = q_bits.shape
+    hkv = k_data.shape[0]
+    G = hq // hkv
+    queries = list(range(nq)) if queries is None else list(queries)
+    O = np.zeros((len(queries), hq, d))
+    L = np.full((len(queries), hq), -np.inf)
+    for g in range(hkv):
+        Kg = decode_kv(k_data[g], None if k_scale is None else k_scale[g], kv_dtype)
+        Vg = decode_kv(v_data[g], None if v_scale is None else v_scale[g], kv_dtype)
+        for n, i in enumerate(queries):
+            pages = np.asarray(sorted(S[g][i]), dtype=np.int64)
+            t = (pages[:, None] * ps + np.arange(ps)[None, :]).reshape(-1)
+            keep = (t <= int(q_pos[i])) & (t < kv_len)
+            kk = Kg[pages].reshape(-1, d)[keep]
+            vv = Vg[pages].reshape(-1, d)[keep]
+            qh = bf16_bits_to_f64(q_bits[i, g * G:(g + 1) * G])          # [G, d]
+            o, lse = _softmax_pv(sm_scale * (qh @ kk.T), vv)
+            O[n, g * G:(g + 1) * G] = o
+            L[n, g * G:(g + 1) * G] = lse
+    return O, L
+
+
+def route_b(q_bits, k_data, v_data, k_scale, v_scale, kv_dtype: str,
+            S: List[List[frozenset]], groups_per_g: List[List[List[int]]], q_pos,
+            kv_len: int, ps: int, sm_scale: float):
+    """Through group unions: every group's union pages are visited once for all
+    members, and each member masks out pages it did not select and future keys.
+    Returns O fp64 [nq, hq, d], lse [nq, hq]; rows are written by original ID."""
+    nq, hq, d = q_bits.shape
+    hkv = k_data.shape[0]
+    G = hq // hkv
+    O = np.full((nq, hq, d), np.nan)
+    L = np.full((nq, hq), np.nan)
+    for g in range(hkv):
+        Kg = decode_kv(k_data[g], None if k_scale is None else k_scale[g], kv_dtype)
+        Vg = decode_kv(v_data[g], None if v_scale is None else v_scale[g], kv_dtype)
+        for members in groups_per_g[g]:
+            union = sorted(frozenset().union(*(S[g][m] for m in members)))
+            pages = np.asarray(union, dtype=np.int64)
+            t = (pages[:, None] * ps + np.arange(ps)[None, :]).reshape(-1)
+            tok_page = np.repeat(pages, ps)
+            kk = Kg[pages].reshape(-1, d)
+            vv = Vg[pages].reshape(-1, d)
+            for m in members:
+                sel = np.isin(tok_page, np.asarray(sorted(S[g][m]), dtype=np.int64))
+                keep = sel & (t <= int(q_pos[m])) & (t < kv_len)
+                qh = bf16_bits_to_f64(q_bits[m, g * G:(g + 1) * G])
+                o, lse = _softmax_pv(sm_scale * (qh @ kk[keep].T), vv[keep])
+                O[m, g * G:(g + 1) * G] = o
+                L[m, g * G:(g + 1) * G] = lse
+    return O, L
+
+
+def brute_force(q_bits, k_data, v_data, k_scale, v_scale, kv_dtype: str,
+                S: List[List[frozenset]], q_pos, kv_len: int, ps: int, sm_scale: float):
+    """Explicit scalar loops with math.exp over every (query, head, token): tiny inputs only."""
+    nq, hq, d = q_bits.shape
+    hkv, n_pages = k_data.shape[0], k_data.shape[1]
+    G = hq // hkv
+    K = [decode_kv(k_data[g], None if k_scale is None else k_scale[g], kv_dtype).tolist() for g in range(hkv)]
+    V = [decode_kv(v_data[g], None if v_scale is None else v_scale[g], kv_dtype).tolist() for g in range(hkv)]
+    Q = bf16_bits_to_f64(q_bits).tolist()
+    O = [[[0.0] * d for _ in range(hq)] for _ in range(nq)]
+    L = [[-math.inf] * hq for _ in range(nq)]
+    for i in range(nq):
+        for h in range(hq):
+            g = h // G
+            scores = []
+            for t in range(n_pages * ps):
+                if (t // ps) in S[g][i] and t <= q_pos[i] and t < kv_len:
+                    p, r = divmod(t, ps)
+                    dot = 0.0
+                    for c in range(d):
+                        dot += Q[i][h][c] * K[g][p][r][c]
+                    scores.append((sm_scale * dot, p, r))
+            if not scores:
+                continue
+            m = max(s for s, _, _ in scores)
+            den = 0.0
+            acc = [0.0] * d
+            for s, p, r in scores:
+                w = math.exp(s - m)
+                den += w
+                for c in range(d):
+                    acc[c] += w * V[g][p][r][c]
+            O[i][h] = [a / den for a in acc]
+            L[i][h] = m + math.log(den)
+    return np.asarray(O), np.asarray(L)
+
+
+def dense_supports(nq: int, hkv: int, n_pages: int) -> List[List[frozenset]]:
+    """Every query selects every page (TopK = all pages)."""
+    full = frozenset(range(n_pages))
+    return [[full] * nq for _ in range(hkv)]
+
+
+def shared_supports(tables: List[List[int]], nq: int) -> List[List[frozenset]]:
+    """Every query of KV head g attends to the whole per-KV-group table T_g."""
+    return [[frozenset(t)] * nq for t in tables]
+
+
+def nrms(out: np.ndarray, ref: np.ndarray) -> float:
+    """||O - R||_2 / ||R||_2 over all output elements, in percent."""
+    ref = np.asarray(ref, dtype=np.float64)
+    den = float(np.sqrt((ref ** 2).sum()))
+    num = float(np.sqrt(((np.asarray(out, dtype=np.float64) - ref) ** 2).sum()))
+    return 100.0 * num / den if den else 0.0

@@ -1,0 +1,66 @@
+"""The pins bite: plant a plausible mistake in the oracle (CPU only) and check
+that at least one pin test fails on it.
+
+Each mutation edits one line of an oracle function's source, re-executes it
+in a copy of its module namespace and patches it in for the duration of the
+pin; the real oracle is untouched afterwards.
+"""
+import inspect
+import textwrap
+
+import pytest
+
+import test_oracle_attention as A
+import test_oracle_numerics as N
+import test_oracle_prep as P
+from oracle import attention, numerics, prep
+
+
+def _mutant(module, fn_name, old, new):
+    src = textwrap.dedent(inspect.getsource(getattr(module, fn_name)))
+    assert old in src, (fn_name, old)
+    ns = dict(vars(module))
+    exec(compile(src.replace(old, new, 1), module.__file__, "exec"), ns)
+    return ns[fn_name]
+
+
+MUTATIONS = [
+    # (module, function, original text, planted mistake, pin that must fail)
+    (attention, "route_a", "t <= int(q_pos[i])", "t < int(q_pos[i])",
+     lambda: A.test_route_a_equals_brute_force("bf16", 0)),
+    (attention, "route_a", "sm_scale * (qh @ kk.T)", "(qh @ kk.T)",
+     lambda: A.test_route_a_equals_brute_force("bf16", 0)),
+    (attention, "route_a", "q_bits[i, g * G:(g + 1) * G]", "q_bits[i, g:g + G]",
+     lambda: A.test_dense_support_equals_library_attention("bf16")),
+    (attention, "route_a", "(t < kv_len)", "(t <= kv_len)",
+     lambda: A.test_dense_support_positions_past_cache_end()),
+    (attention, "route_a", "Kg[pages].reshape(-1, d)[keep]", "Kg[pages].reshape(-1, d)[::-1][keep]",
+     lambda: A.test_route_a_equals_brute_force("fp8", 1)),
+    (attention, "_softmax_pv", "(e @ v) / l", "(e @ v)",
+     lambda: A.test_closed_form_zero_query_is_mean()),
+    (attention, "route_b", "sel & (t <= int(q_pos[m]))", "(t <= int(q_pos[m]))",
+     lambda: A.test_grouping_invariance_route_b("bf16")),
+    (numerics, "e4m3fn_value", "e - 7", "e - 8",
+     lambda: N.test_e4m3fn_special_values()),
+    (prep, "group_affinity", "score > best_score", "score >= best_score",
+     lambda: P.test_fig2_printed_counts()),
+    (prep, "group_affinity", "(bits_g[c] & union)", "(bits_g[c] & bits_g[seed])",
+     lambda: P.test_group_hand_trace_union_not_seed()),
+    (prep, "group_affinity", "seed = remaining.pop(0)", "seed = remaining.pop()",
+     lambda: P.test_group_special_cases()),
+    (prep, "union_stats", "slots += n * len(members)", "slots += n",
+     lambda: P.test_fig2_printed_counts()),
+    (prep, "union_tables", "qm |= 1 << j", "qm |= 1 << (len(members) - 1 - j)",
+     lambda: P.test_union_tables_set_algebra()),
+]
+
+
+@pytest.mark.parametrize("module,fn,old,new,pin", MUTATIONS,
+                         ids=[f"{m[1]}:{m[3]}" for m in MUTATIONS])
+def test_pin_catches_planted_mistake(monkeypatch, module, fn, old, new, pin):
+    monkeypatch.setattr(module, fn, _mutant(module, fn, old, new))
+    if module is numerics and fn == "e4m3fn_value":
+        monkeypatch.setattr(numerics, "E4M3FN_TABLE",
+                            numerics.np.array([numerics.e4m3fn_value(c) for c in range(256)]))
+    with pytest.raises(AssertionError):
+        pin()

@@ -1,0 +1,185 @@
+"""Pins for the oracle's preparation steps: bitsets, grouping, union tables, statistics.
+
+The printed pin is PageWeaver's Fig. 2 caption (fixture under tests/golden);
+the rest are hand traces, special cases, invariants, a brute-force optimality
+check of every greedy pick and set algebra written independently of the
+oracle's bit arithmetic.
+"""
+import os
+import random
+
+import numpy as np
+import pytest
+
+from oracle import prep
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load_fig2():
+    spec = {"support": {}}
+    with open(os.path.join(GOLDEN, "fig2_regrouping.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            if key == "support":
+                spec["support"][int(vals[0])] = [int(v) for v in vals[1:]]
+            elif key == "regrouped_groups":
+                spec[key] = [[int(x) for x in v.split(",")] for v in vals]
+            else:
+                spec[key] = int(vals[0])
+    nq = len(spec["support"])
+    topk = np.array([[spec["support"][i]] for i in range(nq)], dtype=np.int32)  # [nq, 1, 2]
+    return spec, topk
+
+
+def test_fig2_printed_counts():
+    spec, topk = load_fig2()
+    bits = prep.page_bitsets(topk, spec["n_pages"])
+    nq = topk.shape[0]
+    orig = [prep.group_original(nq, spec["max_group"])]
+    aff = [prep.group_affinity(bits[0], spec["window"], spec["max_group"])]
+    s_orig = prep.union_stats(bits, orig)
+    s_aff = prep.union_stats(bits, aff)
+    assert s_orig["visits"] == spec["original_visits"]
+    assert s_orig["masked"] == spec["original_masked"]
+    assert s_aff["visits"] == spec["regrouped_visits"]
+    assert s_aff["masked"] == spec["regrouped_masked"]
+    assert s_orig["selected"] == s_aff["selected"] == spec["selected_edges"]
+    assert aff[0] == spec["regrouped_groups"]
+
+
+def _sets(topk, g=0):
+    return [frozenset(int(x) for x in row if x >= 0) for row in topk[:, g]]
+
+
+def test_bitsets_match_sets_and_words():
+    rng = np.random.default_rng(1)
+    n_pages = 150
+    topk = rng.integers(-3, n_pages, size=(40, 3, 12)).astype(np.int32)
+    topk[:, :, 5] = topk[:, :, 4]                                 # duplicates collapse
+    bits = prep.page_bitsets(topk, n_pages)
+    words = prep.bits_to_words(bits, n_pages)
+    assert words.shape == (3, 40, 3)
+    for g in range(3):
+        for i, s in enumerate(_sets(topk, g)):
+            got = {p for p in range(n_pages) if (int(words[g, i, p // 64]) >> (p % 64)) & 1}
+            assert got == set(s)
+
+
+def test_bitsets_reject_out_of_range():
+    topk = np.array([[[0, 5]]], dtype=np.int32)
+    with pytest.raises(ValueError):
+        prep.page_bitsets(topk, 5)
+
+
+def test_num_groups():
+    assert prep.num_groups(256, 64, 8) == 32
+    assert prep.num_groups(70, 64, 8) == 8 + 1
+    assert prep.num_groups(75, 64, 8) == 8 + 2
+    assert prep.num_groups(5, 64, 8) == 1
+    assert prep.num_groups(0, 64, 8) == 0
+
+
+def _bits_of(sets):
+    return [sum(1 << p for p in s) for s in sets]
+
+
+def test_group_hand_trace():
+    # window of 6, groups of 3.
+    # 0:{1,2,3} 1:{7} 2:{2,3} 3:{1,9} 4:{7,8} 5:{3}
+    # seed 0, U={1,2,3}: overlaps 1:0 2:2 3:1 4:0 5:1 -> 2; U={1,2,3}
+    #   overlaps 1:0 3:1 4:0 5:1 -> 3 (tie with 5, lower ID); group (0,2,3)
+    # seed 1, U={7}: 4:1 5:0 -> 4; then 5 (only one left); group (1,4,5)
+    sets = [{1, 2, 3}, {7}, {2, 3}, {1, 9}, {7, 8}, {3}]
+    assert prep.group_affinity(_bits_of(sets), 6, 3) == [[0, 2, 3], [1, 4, 5]]
+
+
+def test_group_hand_trace_union_not_seed():
+    # The score is overlap with the current union, not with the seed.
+    # seed 0={1}; 1={6} 2={1,5} 3={5}: pick 2 (overlap 1), U={1,5};
+    # then 3 (overlap 1 via page 5) beats 1 (0).  Scoring against the seed
+    # alone would tie 1 and 3 at 0 and take 1.
+    sets = [{1}, {6}, {1, 5}, {5}]
+    assert prep.group_affinity(_bits_of(sets), 4, 3) == [[0, 2, 3], [1]]
+
+
+def test_group_special_cases():
+    same = _bits_of([{1, 2}] * 19)
+    assert prep.group_affinity(same, 8, 4) == [[0, 1, 2, 3], [4, 5, 6, 7], [8, 9, 10, 11],
+                                                [12, 13, 14, 15], [16, 17, 18]]
+    disjoint = _bits_of([{i} for i in range(10)])
+    assert prep.group_affinity(disjoint, 8, 3) == [[0, 1, 2], [3, 4, 5], [6, 7], [8, 9]]
+    assert prep.group_original(10, 4) == [[0, 1, 2, 3], [4, 5, 6, 7], [8, 9]]
+
+
+def _check_greedy_optimal(sets, groups, window, max_group):
+    """Every pick is the argmax over the candidates still free at that moment."""
+    nq = len(sets)
+    for start in range(0, nq, window):
+        free = list(range(start, min(start + window, nq)))
+        wgroups = [g for g in groups if start <= g[0] < start + window]
+        for members in wgroups:
+            assert members[0] == min(free)
+            free.remove(members[0])
+            union = set(sets[members[0]])
+            for c in members[1:]:
+                best = max(len(sets[x] & union) for x in free)
+                assert len(sets[c] & union) == best
+                assert c == min(x for x in free if len(sets[x] & union) == best)
+                free.remove(c)
+                union |= sets[c]
+            assert len(members) == max_group or not free
+        assert not free
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_group_invariants_and_bruteforce(seed):
+    rng = random.Random(seed)
+    nq = rng.randint(1, 90)
+    window = rng.choice([8, 16, 64])
+    max_group = rng.choice([m for m in (1, 2, 4, 8) if window % m == 0])
+    sets = [frozenset(rng.sample(range(40), rng.randint(0, 6))) for _ in range(nq)]
+    groups = prep.group_affinity(_bits_of(sets), window, max_group)
+    flat = sorted(q for g in groups for q in g)
+    assert flat == list(range(nq))                                    # partition
+    assert all(1 <= len(g) <= max_group for g in groups)
+    assert all(len({q // window for q in g}) == 1 for g in groups)    # never crosses a window
+    assert len(groups) == prep.num_groups(nq, window, max_group)
+    _check_greedy_optimal(sets, groups, window, max_group)
+
+
+def test_union_tables_set_algebra():
+    rng = random.Random(3)
+    hkv, nq, n_pages, mg = 2, 37, 130, 4
+    S = [[frozenset(rng.sample(range(n_pages), rng.randint(0, 9))) for _ in range(nq)] for _ in range(hkv)]
+    bits = [_bits_of(s) for s in S]
+    groups = [prep.group_affinity(b, 16, mg) for b in bits]
+    off, pages, qmask = prep.union_tables(bits, groups)
+    e = 0
+    for g in range(hkv):
+        for members in groups[g]:
+            union = sorted(frozenset().union(*(S[g][m] for m in members)))
+            assert list(pages[off[e]:off[e + 1]]) == union
+            for k, p in enumerate(union):
+                want = sum(1 << j for j, m in enumerate(members) if p in S[g][m])
+                assert qmask[off[e] + k] == want
+            e += 1
+    assert off[0] == 0 and off[-1] == len(pages)
+    distinct = sum(len(frozenset().union(*S[g])) for g in range(hkv))
+    assert off[-1] >= distinct
+
+
+def test_stats_definitions():
+    S = [[{0, 1}, {1, 2}, {5}]]
+    bits = [_bits_of(S[0])]
+    st = prep.union_stats(bits, [[[0, 1], [2]]])
+    assert st == {"visits": 3 + 1, "slots": 3 * 2 + 1, "selected": 5, "masked": 2,
+                  "masked_frac": 2 / 7}
+
+
+def test_block_tables_union():
+    rows = np.array([[[0, 3, -1]], [[3, 7, 9]], [[-1, -1, 2]]], dtype=np.int32)
+    assert prep.block_tables(rows, 10) == [[0, 2, 3, 7, 9]]
