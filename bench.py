@@ -1,0 +1,258 @@
+"""Sparse-prefill benchmark: queries/s and unique-KV HBM GB/s on one MI355X.
+
+One step = one complete sparse-prefill call on one chunk of synthetic input:
+page bitsets -> affinity grouping -> union tables -> union attention.  The
+default workload is the long-context fp8 case (64K context, 4096-query chunk,
+Hq=32, Hkv=8, d=128, 64-token pages, Top16 per (query, KV head), OCP e4m3 KV
+with per-page fp32 scales).  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line.  ``roofline`` refers to the attention kernel (the
+dominant one): achieved = unique-KV bytes (every group's union pages, K and V
+plus their scales) / the kernel's mean duration from HIP events on its own
+stream.  ``cpu_baseline`` times the CPU oracle on a bounded sample (the first
+windows of the chunk), single-threaded.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "sparse-prefill queries/s + unique-KV HBM GB/s (% roofline), 64K ctx Top16 fp8"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3_long_fp8")
+    ap.add_argument("--window", type=int, default=None)
+    ap.add_argument("--flush-steps", type=int, default=20,
+                    help="extra steps timed one by one after writing 512 MiB (L2/MALL flush)")
+    ap.add_argument("--cpu-queries", type=int, default=256,
+                    help="oracle sample: the first N queries (whole windows), all KV heads")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=None,
+                    help="run only this many steps after warmup (for rocprofv3), no extras")
+    return ap.parse_args()
+
+
+def unique_kv_bytes(union_pages_total: int, cfg) -> int:
+    esz = 1 if cfg.kv_dtype == "fp8" else 2
+    per_page = 2 * cfg.ps * cfg.d * esz + (8 if cfg.kv_dtype == "fp8" else 0)
+    return union_pages_total * per_page
+
+
+def cpu_baseline(w, n_queries: int) -> dict:
+    """The oracle as it stands on the first n_queries queries (whole windows), 1 thread."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention, prep
+    cfg = w.cfg
+    nqs = min(cfg.nq, max(cfg.window, (n_queries // cfg.window) * cfg.window))
+    topk = w.topk[:nqs]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        bits = prep.page_bitsets(topk, cfg.n_pages)
+        groups = [prep.group_affinity(b, cfg.window, cfg.max_group) for b in bits]
+        prep.union_tables(bits, groups)
+        t1 = time.perf_counter()
+        S = prep.supports(topk, cfg.n_pages)
+        attention.route_a(w.q[:nqs], w.k, w.v, w.k_scale, w.v_scale, cfg.kv_dtype, S, w.q_pos[:nqs],
+                          cfg.kv_len, cfg.ps, 1.0 / math.sqrt(cfg.d))
+        t2 = time.perf_counter()
+    return {"value": nqs / (t2 - t0), "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {nqs} of {cfg.nq} queries ({nqs // cfg.window} windows of {cfg.window}), "
+                      f"all {cfg.hkv} KV heads; prep {t1 - t0:.2f}s + attention {t2 - t1:.2f}s",
+            "cpu": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path runs on a single MI355X with no sharding; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import query_union_kv_amd as pw
+    from workloads import CONFIGS, make_workload
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    cfg = CONFIGS[args.workload]
+    if args.window:
+        cfg = cfg.scaled(window=args.window)
+    w = make_workload(cfg)
+    dev = torch.device("cuda:0")
+
+    q = torch.from_numpy(w.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    if cfg.kv_dtype == "bf16":
+        kc = torch.from_numpy(w.k.view(np.int16)).view(torch.bfloat16).to(dev)
+        vc = torch.from_numpy(w.v.view(np.int16)).view(torch.bfloat16).to(dev)
+        ks = vs = None
+    else:
+        kc, vc = torch.from_numpy(w.k).to(dev), torch.from_numpy(w.v).to(dev)
+        ks, vs = torch.from_numpy(w.k_scale).to(dev), torch.from_numpy(w.v_scale).to(dev)
+    q_pos = torch.from_numpy(w.q_pos).to(dev)
+    ids_np = w.topk if w.topk is not None else w.mask_rows
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np)).to(dev)
+    mode = "topk" if w.topk is not None else "block_union"
+    plan = pw.SparsePrefill(nq=cfg.nq, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, n_pages=cfg.n_pages,
+                            page_size=cfg.ps, kv_len=cfg.kv_len, k=ids.shape[2], window=cfg.window,
+                            max_group=cfg.max_group, mode=mode,
+                            n_rows=ids.shape[0] if mode == "block_union" else 0, device=dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        plan.prepare(ids, stream)
+        if evs:
+            evs[1].record(stream)
+        plan.attend(q, kc, vc, q_pos, out, ks, vs, stream=stream)
+        if evs:
+            evs[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    if args.profile_steps is not None:
+        for _ in range(args.profile_steps):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps, "workload": cfg.name}))
+        return
+
+    # ---- the timed region: K complete steps back to back -------------------------------
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_prep = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)]
+    t_attn = [evs[i][1].elapsed_time(evs[i][2]) for i in range(args.steps)]
+    ms_step = wall * 1e3 / args.steps
+    value = cfg.nq / (ms_step / 1e3)
+
+    # ---- structure of this call's tables --------------------------------------------------
+    off = plan.union_off.cpu().numpy()
+    total_pages = int(off[-1])
+    Bu = unique_kv_bytes(total_pages, cfg)
+    attn_ms = statistics.mean(t_attn)
+    achieved = Bu / (attn_ms / 1e3) / 1e9
+    extras = {"t_prep_ms_mean": statistics.mean(t_prep), "t_attn_ms_mean": attn_ms,
+              "t_attn_ms_median": statistics.median(t_attn), "union_pages": total_pages,
+              "unique_kv_bytes": Bu}
+    if mode == "topk":
+        sizes = np.diff(off)
+        gsz = plan.group_size.cpu().numpy().reshape(-1)
+        qm = plan.union_qmask[:total_pages].cpu().numpy()
+        selected = int(np.unpackbits(qm[:, None], axis=1).sum())      # retained selected edges
+        slots = int((sizes * gsz).sum())                                # member x union-page slots
+        orig = pw.SparsePrefill(nq=cfg.nq, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, n_pages=cfg.n_pages,
+                                page_size=cfg.ps, kv_len=cfg.kv_len, k=ids.shape[2], window=cfg.window,
+                                max_group=cfg.max_group, grouping="original", device=dev)
+        orig.prepare(ids)
+        torch.cuda.synchronize()
+        orig_pages = int(orig.union_off[-1].item())
+        per_q = cfg.nq * cfg.hkv
+        extras.update({
+            "visits_per_query_kvh": {"per_query": selected / per_q, "original_union": orig_pages / per_q,
+                                     "affinity_union": total_pages / per_q},
+            "masked_slot_frac": (slots - selected) / slots if slots else 0.0,
+            "selected_edges": selected,
+        })
+
+        def timed(fn, n=10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            fn()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+
+        # Fig. 6 / Eq. 7 decomposition: original-order Union call, attention over fixed
+        # affinity tables, and the complete online affinity call.
+        t_orig = timed(lambda: (orig.prepare(ids, stream),
+                                orig.attend(q, kc, vc, q_pos, out, ks, vs, stream=stream)))
+        t_orig_attn = timed(lambda: orig.attend(q, kc, vc, q_pos, out, ks, vs, stream=stream))
+        t_fixed = timed(lambda: plan.attend(q, kc, vc, q_pos, out, ks, vs, stream=stream))
+        t_online = timed(lambda: step())
+        extras["fig6_ms"] = {"original_union_call": t_orig, "original_union_attention": t_orig_attn,
+                             "fixed_affinity_attention": t_fixed, "online_affinity_call": t_online,
+                             "execution_saving": t_orig_attn - t_fixed,
+                             "online_cost": t_online - t_fixed, "net_saving": t_orig - t_online}
+        exec_rows_pages = float((sizes * gsz).sum()) * cfg.g     # (row, union page) pairs
+    else:
+        exec_rows_pages = float(total_pages) * cfg.nq * cfg.g    # every row of a KV head x its table
+    # executed MFMA work: QK and PV, 2 flops per MAC, over every (row, union token)
+    exec_flops = 4.0 * cfg.d * cfg.ps * exec_rows_pages
+    extras["executed_tflops"] = exec_flops / (attn_ms / 1e3) / 1e12
+    extras["attn_queries_per_s"] = cfg.nq / (attn_ms / 1e3)
+
+    # ---- flushed timing: 512 MiB written before each step, outside the event pair ----------
+    if args.flush_steps:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        fl = []
+        for _ in range(args.flush_steps):
+            scratch.fill_(1)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            step(e)
+            torch.cuda.synchronize()
+            fl.append((e[0].elapsed_time(e[2]), e[1].elapsed_time(e[2])))
+        del scratch
+        f_call = statistics.median(x[0] for x in fl)
+        f_attn = statistics.median(x[1] for x in fl)
+        extras["flushed"] = {"ms_per_call_median": f_call, "attn_ms_median": f_attn,
+                             "queries_per_s": cfg.nq / (f_call / 1e3),
+                             "unique_kv_GBs": Bu / (f_attn / 1e3) / 1e9}
+
+    rec = {
+        "metric": METRIC, "value": value, "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "hq": cfg.hq, "hkv": cfg.hkv, "d": cfg.d, "page_size": cfg.ps,
+                   "kv_len": cfg.kv_len, "nq": cfg.nq, "topk": cfg.k, "kv_dtype": cfg.kv_dtype,
+                   "window": cfg.window, "max_group": cfg.max_group, "seed": w.seed},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "k_attn",
+                     "bytes_per_launch": Bu},
+        "extra": extras,
+    }
+    if not args.no_cpu and mode == "topk":
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_queries)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

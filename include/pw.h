@@ -1,0 +1,174 @@
+/* pw.h - query-union sparse-attention prefill on AMD Instinct MI355X (gfx950).
+ *
+ * Sparse prefill in which every query keeps its own TopK set of KV-cache
+ * pages (its support), queries are grouped by selected-page affinity, each
+ * group's page union is read once, and causal online-softmax attention runs
+ * for every query over exactly its own pages, each output row written to the
+ * query's original ID ("PageWeaver: KV-Guided Query Unions for Sparse
+ * Attention", abstract and Figs. 1-3; "CompactAttention: Accelerating Chunked
+ * Prefill with Block-Union KV Selection", summary "Approach").
+ *
+ * Conventions for every entry point
+ *  - C ABI.  Arrays are row-major, sizes are int32 unless noted, and every
+ *    array argument is a DEVICE pointer unless noted.
+ *  - The caller allocates and frees every buffer.  The library keeps no device
+ *    state between calls, never allocates device memory and never
+ *    synchronises: each call validates its scalar arguments on the host,
+ *    enqueues its kernels on `stream` (NULL = the null stream) and returns.
+ *  - On any non-OK status nothing has been enqueued and outputs are untouched;
+ *    pw_last_error() returns a thread-local message explaining why.
+ *  - Support content rules (shared by every step): page IDs < 0 are empty
+ *    slots, duplicate IDs collapse (a support is a set), IDs >= n_pages are
+ *    ignored and counted (pw_page_bitsets).  A page wholly after a query's
+ *    position is legal; its keys are causally masked.
+ *  - Thread safety: calls are independent; the library has no global state
+ *    other than the per-thread error text.
+ */
+#ifndef PW_H_
+#define PW_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int pw_status;
+#define PW_OK 0
+#define PW_ERR_ARG (-1)         /* bad size, null pointer or inconsistent arguments   */
+#define PW_ERR_UNSUPPORTED (-2) /* valid request outside what the kernels implement   */
+#define PW_ERR_CAPACITY (-3)    /* an output buffer is smaller than its required size */
+#define PW_ERR_HIP (-4)         /* a HIP launch or runtime call failed                */
+
+/* KV cache element types. */
+#define PW_KV_BF16 0     /* bfloat16                                                       */
+#define PW_KV_FP8_E4M3 1 /* OCP fp8 E4M3 ("e4m3fn": bias 7, max 448, no inf) with an fp32
+                            scale per (KV head, page) for K and for V; value = code*scale. */
+
+/* ---- host helpers (no device work) ------------------------------------------------ */
+
+/* Version string of the library. */
+const char* pw_version(void);
+
+/* Text of the last non-OK status returned on this thread ("" if none). */
+const char* pw_last_error(void);
+
+/* 64-bit words per page bitset row: ceil(n_pages / 64). */
+int pw_words(int n_pages);
+
+/* Groups per KV head produced by pw_group: each window of `window`
+ * consecutive query IDs yields ceil(len / max_group) groups.  -1 on bad args. */
+int pw_num_groups(int nq, int window, int max_group);
+
+/* Minimum `capacity` (entries) of union_pages / union_qmask for pw_union_tables:
+ * n_tables * min(n_pages, group_width * k_max), where k_max bounds every row's
+ * support size.  -1 on bad args. */
+int64_t pw_union_capacity(int n_tables, int group_width, int k_max, int n_pages);
+
+/* ---- (1) page bitsets -------------------------------------------------------------
+ * PageWeaver Fig. 1: fixed TopK pages per query guide the regrouping.  Row r of
+ * KV head g becomes a bitset with bit p set iff page p is in the support, built
+ * by wavefront ballots (one 64-page word per ballot).
+ *
+ * topk          int32 [n_rows][hkv][k]         page IDs, -1 = empty slot
+ * bits          uint64 [hkv][n_rows][pw_words(n_pages)]   output, bit p in word p/64
+ * bad_id_count  int32 [1] or NULL: incremented once per ID >= n_pages (caller zeroes it)
+ * Limits: n_rows >= 0, hkv >= 1, 1 <= k <= 4096, 1 <= n_pages <= 65536.            */
+pw_status pw_page_bitsets(const int32_t* topk, int n_rows, int hkv, int k, int n_pages,
+                          uint64_t* bits, int32_t* bad_id_count, hipStream_t stream);
+
+/* ---- (2) bounded affinity grouping --------------------------------------------------
+ * PageWeaver abstract and Figs. 1-2: a bounded GPU search over selected-page
+ * affinity produces query IDs; original IDs keep support, position and output
+ * address.  Rule: per KV head, disjoint windows of `window` consecutive query
+ * IDs are grouped independently; the seed is the lowest ungrouped ID; the group
+ * repeatedly takes the ungrouped candidate with the largest overlap
+ * popcount(bits[c] & U) with its current union U (ties -> lower ID; zero
+ * overlap still joins) until it has max_group members or the window is empty.
+ *
+ * bits        uint64 [hkv][nq][pw_words(n_pages)]  (from pw_page_bitsets)
+ * group_qids  int32 [hkv][G][max_group] output, G = pw_num_groups(nq, window, max_group);
+ *             members in pick order, -1 padded.  Groups are ordered by window,
+ *             then creation.
+ * group_size  int32 [hkv][G] output, 1..max_group.
+ * Limits: 1 <= max_group <= 8, window % max_group == 0, window <= 1024,
+ *         n_pages <= 4096.                                                          */
+pw_status pw_group(const uint64_t* bits, int nq, int hkv, int n_pages, int window,
+                   int max_group, int32_t* group_qids, int32_t* group_size, hipStream_t stream);
+
+/* ---- (3) union tables -----------------------------------------------------------------
+ * PageWeaver Fig. 2 (a group's union is visited once, members keep their own
+ * pages) and CompactAttention "Approach" (Q-block and intra-group head unions
+ * give a per-KV-group block table).  For every table e = g * n_groups + j the
+ * union of the member rows' bitsets is listed in ascending page order, built by
+ * popcount, prefix sum and compaction.
+ *
+ * bits         uint64 [hkv][n_rows][pw_words(n_pages)]
+ * group_rows   int32 [hkv][n_groups][group_width]: row indices (-1 padded); member j
+ *              of a table is group_rows[..][j]
+ * group_size   int32 [hkv][n_groups] or NULL (then every table has group_width members)
+ * union_off    int32 [hkv*n_groups + 1] output: exclusive prefix sum of union sizes
+ * union_pages  int32 [capacity] output: pages of table e at [union_off[e], union_off[e+1])
+ * union_qmask  uint8 [capacity] output or NULL: bit j set iff member j selected the page;
+ *              requires group_width <= 8
+ * capacity     entries available; must be >= pw_union_capacity(hkv*n_groups,
+ *              group_width, k_max, n_pages).  Entries past capacity are never
+ *              written (defensive clamp if k_max understated the supports).
+ * Limits: 1 <= group_width <= 64, n_pages <= 65536.                                  */
+pw_status pw_union_tables(const uint64_t* bits, int n_rows, int hkv, int n_pages,
+                          const int32_t* group_rows, const int32_t* group_size, int n_groups,
+                          int group_width, int k_max, int32_t* union_off, int32_t* union_pages,
+                          uint8_t* union_qmask, int64_t capacity, hipStream_t stream);
+
+/* ---- (4) ID-aware union attention -----------------------------------------------------
+ * PageWeaver abstract, Fig. 1 and Fig. 3: each group's union pages are staged
+ * on chip once; for every member the same lanes compute QK, the masked online
+ * softmax and PV, keeping the member's state and writing its rows to its
+ * original ID, with no reordered Q and no cross-page partial outputs.
+ * CompactAttention "Approach": attention runs in place over the paged cache in
+ * KV-head-major layout.
+ *
+ * Work item (g, j) = KV head g, group j: rows (member m, head h) for the
+ * members m of the group and h in [g*G, (g+1)*G), G = hq / hkv.  For every union
+ * page P of the item's table and every token t = P*page_size + s of it, key t
+ * is used by member m iff m selected P (union_qmask bit, or always when
+ * union_qmask is NULL), t <= q_pos[m] and t < kv_len.  Output
+ *   out[m][h][:] = sum_t softmax_t(sm_scale * q[m][h] . K[g][t]) V[g][t]
+ * rounded to bf16 (0 when no key is used), lse[m][h] = natural-log sum-exp
+ * of the scaled scores (-inf when no key is used).
+ *
+ * q           bf16 [nq][hq][d]
+ * k_cache     [hkv][*][page_size][d] element type kv_dtype; page P of head g at
+ * v_cache       byte offset (g*stride_head + P*stride_page) * elem_size, the d
+ *             elements of a token contiguous, tokens of a page contiguous
+ * k_scale     fp32 [hkv][n_pages] (fp8 only, else NULL); same for v_scale
+ * q_pos       int32 [nq] absolute position of each query
+ * group_qids  int32 [hkv][n_groups][max_group] (-1 padded) or NULL: then group j
+ *             is the consecutive IDs [j*max_group, min((j+1)*max_group, nq))
+ * group_size  int32 [hkv][n_groups] (required iff group_qids != NULL)
+ * shared_table 0: item (g, j) uses table g*n_groups + j;
+ *             1: every item of KV head g uses table g (a per-KV-group block table)
+ * union_off / union_pages / union_qmask: tables as written by pw_union_tables
+ *             (union_qmask NULL = every member uses every page of its table)
+ * capacity    entries in union_pages (reads are clamped to it)
+ * out         bf16 [nq][hq][d]; each row written exactly once if it belongs to
+ *             a group; rows of queries in no group are left untouched
+ * lse         fp32 [nq][hq] or NULL
+ * Limits: d in {64, 128}; page_size in {64, 128}; hq % hkv == 0;
+ *         G * max_group <= 64; 1 <= max_group <= 8; n_pages >= 1.                   */
+pw_status pw_sparse_prefill(const void* q, int nq, int hq, int hkv, int d,
+                            const void* k_cache, const void* v_cache, int kv_dtype,
+                            const float* k_scale, const float* v_scale, int page_size,
+                            int n_pages, int64_t stride_head, int64_t stride_page,
+                            const int32_t* q_pos, int kv_len, float sm_scale,
+                            const int32_t* group_qids, const int32_t* group_size, int n_groups,
+                            int max_group, int shared_table, const int32_t* union_off,
+                            const int32_t* union_pages, const uint8_t* union_qmask,
+                            int64_t capacity, void* out, float* lse, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PW_H_ */

@@ -1,0 +1,277 @@
+"""Python binding of libpw.so: query-union sparse-attention prefill on MI355X.
+
+The functions below carry the C-ABI entry points' names and only marshal
+arguments: they check tensor devices, dtypes, shapes and contiguity, pass raw
+device pointers and the current HIP stream, and raise ``PWError`` on a non-OK
+status.  Every step of the path runs in the library's HIP kernels; PyTorch
+provides device memory and streams.  There is no fallback: if the library is
+missing or no GPU is present the calls fail.
+
+``SparsePrefill`` chains the four calls for one workload shape and owns the
+intermediate buffers (bitsets, groups, union tables).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "PWError", "lib", "pw_version", "pw_words", "pw_num_groups", "pw_union_capacity",
+    "pw_page_bitsets", "pw_group", "pw_union_tables", "pw_sparse_prefill", "SparsePrefill",
+    "PW_KV_BF16", "PW_KV_FP8_E4M3", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpw.so")
+PW_KV_BF16 = 0
+PW_KV_FP8_E4M3 = 1
+_STATUS = {0: "PW_OK", -1: "PW_ERR_ARG", -2: "PW_ERR_UNSUPPORTED", -3: "PW_ERR_CAPACITY",
+           -4: "PW_ERR_HIP"}
+
+
+class PWError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libpw.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        sig = {
+            "pw_version": (ctypes.c_char_p, []),
+            "pw_last_error": (ctypes.c_char_p, []),
+            "pw_words": (I, [I]),
+            "pw_num_groups": (I, [I, I, I]),
+            "pw_union_capacity": (I64, [I, I, I, I]),
+            "pw_page_bitsets": (I, [P, I, I, I, I, P, P, P]),
+            "pw_group": (I, [P, I, I, I, I, I, P, P, P]),
+            "pw_union_tables": (I, [P, I, I, I, P, P, I, I, I, P, P, P, I64, P]),
+            "pw_sparse_prefill": (I, [P, I, I, I, I, P, P, I, P, P, I, I, I64, I64, P, I, F,
+                                      P, P, I, I, I, P, P, P, I64, P, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise PWError(status, lib().pw_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor") -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def pw_version() -> str:
+    return lib().pw_version().decode()
+
+
+def pw_words(n_pages: int) -> int:
+    return lib().pw_words(n_pages)
+
+
+def pw_num_groups(nq: int, window: int, max_group: int) -> int:
+    return lib().pw_num_groups(nq, window, max_group)
+
+
+def pw_union_capacity(n_tables: int, group_width: int, k_max: int, n_pages: int) -> int:
+    return lib().pw_union_capacity(n_tables, group_width, k_max, n_pages)
+
+
+def pw_page_bitsets(topk: torch.Tensor, n_pages: int, bits: torch.Tensor,
+                    bad_id_count: Optional[torch.Tensor] = None, stream=None) -> None:
+    """topk int32 [n_rows, hkv, k] -> bits int64 (uint64 words) [hkv, n_rows, words]."""
+    n_rows, hkv, k = topk.shape
+    if tuple(bits.shape) != (hkv, n_rows, pw_words(n_pages)):
+        raise ValueError(f"bits shape {tuple(bits.shape)} != {(hkv, n_rows, pw_words(n_pages))}")
+    _check(lib().pw_page_bitsets(_ptr(topk, torch.int32, "topk"), n_rows, hkv, k, n_pages,
+                                 _ptr(bits, torch.int64, "bits"),
+                                 _ptr(bad_id_count, torch.int32, "bad_id_count"), _stream(stream)))
+
+
+def pw_group(bits: torch.Tensor, n_pages: int, window: int, max_group: int,
+             group_qids: torch.Tensor, group_size: torch.Tensor, stream=None) -> None:
+    """bits [hkv, nq, words] -> group_qids int32 [hkv, G, max_group], group_size int32 [hkv, G]."""
+    hkv, nq, _ = bits.shape
+    n_groups = pw_num_groups(nq, window, max_group)
+    if tuple(group_qids.shape) != (hkv, n_groups, max_group) or tuple(group_size.shape) != (hkv, n_groups):
+        raise ValueError("group_qids/group_size shapes do not match pw_num_groups")
+    _check(lib().pw_group(_ptr(bits, torch.int64, "bits"), nq, hkv, n_pages, window, max_group,
+                          _ptr(group_qids, torch.int32, "group_qids"),
+                          _ptr(group_size, torch.int32, "group_size"), _stream(stream)))
+
+
+def pw_union_tables(bits: torch.Tensor, n_pages: int, group_rows: torch.Tensor,
+                    group_size: Optional[torch.Tensor], k_max: int, union_off: torch.Tensor,
+                    union_pages: torch.Tensor, union_qmask: Optional[torch.Tensor] = None,
+                    stream=None) -> None:
+    """bits [hkv, n_rows, words], group_rows int32 [hkv, n_groups, width] -> CSR union tables."""
+    hkv, n_rows, _ = bits.shape
+    _, n_groups, width = group_rows.shape
+    if union_off.numel() != hkv * n_groups + 1:
+        raise ValueError("union_off must have hkv*n_groups+1 entries")
+    if union_qmask is not None and union_qmask.numel() < union_pages.numel():
+        raise ValueError("union_qmask smaller than union_pages")
+    _check(lib().pw_union_tables(_ptr(bits, torch.int64, "bits"), n_rows, hkv, n_pages,
+                                 _ptr(group_rows, torch.int32, "group_rows"),
+                                 _ptr(group_size, torch.int32, "group_size"), n_groups, width, k_max,
+                                 _ptr(union_off, torch.int32, "union_off"),
+                                 _ptr(union_pages, torch.int32, "union_pages"),
+                                 _ptr(union_qmask, torch.uint8, "union_qmask"),
+                                 union_pages.numel(), _stream(stream)))
+
+
+def pw_sparse_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      q_pos: torch.Tensor, kv_len: int, union_off: torch.Tensor,
+                      union_pages: torch.Tensor, out: torch.Tensor, *,
+                      hkv: int, n_groups: int, max_group: int,
+                      group_qids: Optional[torch.Tensor] = None,
+                      group_size: Optional[torch.Tensor] = None,
+                      union_qmask: Optional[torch.Tensor] = None,
+                      k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                      shared_table: bool = False, sm_scale: Optional[float] = None,
+                      lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    """q bf16 [nq, hq, d]; k_cache/v_cache [hkv, n_pages, page_size, d] (bf16 or uint8 fp8 codes)."""
+    nq, hq, d = q.shape
+    if k_cache.shape != v_cache.shape or k_cache.dim() != 4 or k_cache.shape[0] != hkv:
+        raise ValueError("k_cache/v_cache must be [hkv, n_pages, page_size, d]")
+    _, n_pages, page_size, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("head dim mismatch")
+    if k_cache.dtype == torch.bfloat16:
+        kv_dtype = PW_KV_BF16
+    elif k_cache.dtype in (torch.uint8, torch.float8_e4m3fn):
+        kv_dtype = PW_KV_FP8_E4M3
+    else:
+        raise ValueError(f"unsupported cache dtype {k_cache.dtype}")
+    if out.shape != q.shape or out.dtype != torch.bfloat16:
+        raise ValueError("out must be bf16 shaped like q")
+    sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    _check(lib().pw_sparse_prefill(
+        _ptr(q, torch.bfloat16, "q"), nq, hq, hkv, d, _ptr(k_cache, name="k_cache"),
+        _ptr(v_cache, name="v_cache"), kv_dtype, _ptr(k_scale, torch.float32, "k_scale"),
+        _ptr(v_scale, torch.float32, "v_scale"), page_size, n_pages, n_pages * page_size * d,
+        page_size * d, _ptr(q_pos, torch.int32, "q_pos"), kv_len, sm,
+        _ptr(group_qids, torch.int32, "group_qids"), _ptr(group_size, torch.int32, "group_size"),
+        n_groups, max_group, 1 if shared_table else 0, _ptr(union_off, torch.int32, "union_off"),
+        _ptr(union_pages, torch.int32, "union_pages"), _ptr(union_qmask, torch.uint8, "union_qmask"),
+        union_pages.numel(), _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"),
+        _stream(stream)))
+
+
+@dataclass
+class SparsePrefill:
+    """The four calls of one complete sparse-prefill call, with their buffers.
+
+    Per-query mode (``topk`` given): page bitsets -> affinity grouping (or
+    original-order groups when ``grouping='original'``) -> union tables with
+    member masks -> union attention.
+    Block-union mode (``mask_rows`` given, CompactAttention's per-KV-group
+    block table): bitsets of the mask rows -> one union over every row of a
+    KV head -> attention of consecutive query groups over that shared table.
+    """
+    nq: int
+    hq: int
+    hkv: int
+    d: int
+    n_pages: int
+    page_size: int
+    kv_len: int
+    k: int                      # ids per row of topk / mask_rows
+    window: int = 64
+    max_group: int = 8
+    mode: str = "topk"          # "topk" or "block_union"
+    grouping: str = "affinity"  # "affinity" or "original" (topk mode)
+    n_rows: int = 0             # block_union: mask rows per KV head
+    device: str = "cuda"
+
+    def __post_init__(self):
+        dev = self.device
+        w = pw_words(self.n_pages)
+        i32 = dict(dtype=torch.int32, device=dev)
+        if self.mode == "topk":
+            self.n_rows = self.nq
+            self.n_groups = pw_num_groups(self.nq, self.window, self.max_group)
+            self.width = self.max_group
+            n_tables = self.hkv * self.n_groups
+        elif self.mode == "block_union":
+            self.n_groups = -(-self.nq // self.max_group)
+            self.width = self.n_rows
+            n_tables = self.hkv
+        else:
+            raise ValueError(self.mode)
+        self.bits = torch.empty((self.hkv, self.n_rows, w), dtype=torch.int64, device=dev)
+        self.bad_ids = torch.zeros(1, **i32)
+        cap = pw_union_capacity(n_tables, self.width, self.k, self.n_pages)
+        self.union_off = torch.empty(n_tables + 1, **i32)
+        self.union_pages = torch.empty(max(cap, 1), **i32)
+        if self.mode == "topk":
+            self.group_qids = torch.empty((self.hkv, self.n_groups, self.max_group), **i32)
+            self.group_size = torch.empty((self.hkv, self.n_groups), **i32)
+            self.union_qmask = torch.empty(max(cap, 1), dtype=torch.uint8, device=dev)
+            if self.grouping == "original":
+                ids = torch.arange(self.n_groups * self.max_group, **i32).view(self.n_groups, self.max_group)
+                ids = torch.where(ids < self.nq, ids, torch.full_like(ids, -1))
+                self.group_qids.copy_(ids.expand(self.hkv, -1, -1))
+                self.group_size.copy_((ids >= 0).sum(1, dtype=torch.int32).expand(self.hkv, -1))
+        else:
+            self.group_rows = torch.arange(self.n_rows, **i32).view(1, 1, -1).repeat(self.hkv, 1, 1)
+            self.group_qids = self.group_size = self.union_qmask = None
+
+    def prepare(self, ids: torch.Tensor, stream=None) -> None:
+        """Bitsets, grouping and union tables from topk [nq, hkv, k] or mask rows [n_rows, hkv, k]."""
+        pw_page_bitsets(ids, self.n_pages, self.bits, self.bad_ids, stream)
+        if self.mode == "topk":
+            if self.grouping == "affinity":
+                pw_group(self.bits, self.n_pages, self.window, self.max_group, self.group_qids,
+                         self.group_size, stream)
+            pw_union_tables(self.bits, self.n_pages, self.group_qids, self.group_size, self.k,
+                            self.union_off, self.union_pages, self.union_qmask, stream)
+        else:
+            pw_union_tables(self.bits, self.n_pages, self.group_rows, None, self.k,
+                            self.union_off, self.union_pages, None, stream)
+
+    def attend(self, q, k_cache, v_cache, q_pos, out, k_scale=None, v_scale=None, lse=None,
+               sm_scale=None, stream=None) -> None:
+        pw_sparse_prefill(q, k_cache, v_cache, q_pos, self.kv_len, self.union_off, self.union_pages,
+                          out, hkv=self.hkv, n_groups=self.n_groups, max_group=self.max_group,
+                          group_qids=self.group_qids, group_size=self.group_size,
+                          union_qmask=self.union_qmask, k_scale=k_scale, v_scale=v_scale,
+                          shared_table=self.mode == "block_union", sm_scale=sm_scale, lse=lse,
+                          stream=stream)
+
+    def __call__(self, ids, q, k_cache, v_cache, q_pos, out, k_scale=None, v_scale=None, lse=None,
+                 stream=None) -> None:
+        self.prepare(ids, stream)
+        self.attend(q, k_cache, v_cache, q_pos, out, k_scale, v_scale, lse, stream=stream)

@@ -1,0 +1,185 @@
+// C ABI of the query-union sparse-prefill library: host-side validation of every
+// scalar argument, then the kernel launches.  Declarations and argument meaning are
+// in include/pw.h.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+
+#include "common.h"
+
+#define PW_VERSION "0.1.0"
+
+namespace pw {
+namespace {
+thread_local char g_err[512] = "";
+}
+
+pw_status fail(pw_status status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+pw_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PW_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return PW_OK;
+}
+
+}  // namespace pw
+
+using pw::fail;
+
+extern "C" {
+
+const char* pw_version(void) { return PW_VERSION; }
+
+const char* pw_last_error(void) { return pw::g_err; }
+
+int pw_words(int n_pages) { return n_pages < 0 ? -1 : (n_pages + 63) / 64; }
+
+int pw_num_groups(int nq, int window, int max_group) {
+  if (nq < 0 || window < 1 || max_group < 1) return -1;
+  const int full = nq / window, rest = nq % window;
+  const int64_t total = (int64_t)full * ((window + max_group - 1) / max_group) +
+                        (rest + max_group - 1) / max_group;
+  return total > INT32_MAX ? -1 : (int)total;
+}
+
+int64_t pw_union_capacity(int n_tables, int group_width, int k_max, int n_pages) {
+  if (n_tables < 0 || group_width < 1 || k_max < 0 || n_pages < 1) return -1;
+  const int64_t per = std::min<int64_t>(n_pages, (int64_t)group_width * k_max);
+  return (int64_t)n_tables * per;
+}
+
+pw_status pw_page_bitsets(const int32_t* topk, int n_rows, int hkv, int k, int n_pages,
+                          uint64_t* bits, int32_t* bad_id_count, hipStream_t stream) {
+  pw::g_err[0] = 0;
+  if (n_rows < 0 || hkv < 1 || k < 1 || n_pages < 1)
+    return fail(PW_ERR_ARG, "pw_page_bitsets: bad sizes n_rows=%d hkv=%d k=%d n_pages=%d", n_rows,
+                hkv, k, n_pages);
+  if (k > 4096) return fail(PW_ERR_UNSUPPORTED, "pw_page_bitsets: k=%d > 4096", k);
+  if (n_pages > 65536)
+    return fail(PW_ERR_UNSUPPORTED, "pw_page_bitsets: n_pages=%d > 65536", n_pages);
+  if ((int64_t)n_rows * hkv > INT32_MAX)
+    return fail(PW_ERR_UNSUPPORTED, "pw_page_bitsets: n_rows*hkv too large");
+  if (n_rows > 0 && (!topk || !bits)) return fail(PW_ERR_ARG, "pw_page_bitsets: null topk/bits");
+  return pw::launch_page_bitsets(topk, n_rows, hkv, k, n_pages, bits, bad_id_count, stream);
+}
+
+pw_status pw_group(const uint64_t* bits, int nq, int hkv, int n_pages, int window, int max_group,
+                   int32_t* group_qids, int32_t* group_size, hipStream_t stream) {
+  pw::g_err[0] = 0;
+  if (nq < 0 || hkv < 1 || n_pages < 1)
+    return fail(PW_ERR_ARG, "pw_group: bad sizes nq=%d hkv=%d n_pages=%d", nq, hkv, n_pages);
+  if (max_group < 1 || max_group > 8)
+    return fail(PW_ERR_UNSUPPORTED, "pw_group: max_group=%d not in 1..8", max_group);
+  if (window < 1 || window > 1024)
+    return fail(PW_ERR_UNSUPPORTED, "pw_group: window=%d not in 1..1024", window);
+  if (window % max_group)
+    return fail(PW_ERR_ARG, "pw_group: window=%d is not a multiple of max_group=%d", window,
+                max_group);
+  if (n_pages > 4096) return fail(PW_ERR_UNSUPPORTED, "pw_group: n_pages=%d > 4096", n_pages);
+  const int n_groups = pw_num_groups(nq, window, max_group);
+  if (n_groups < 0 || (int64_t)n_groups * hkv * max_group > INT32_MAX)
+    return fail(PW_ERR_UNSUPPORTED, "pw_group: too many groups");
+  if (nq > 0 && (!bits || !group_qids || !group_size))
+    return fail(PW_ERR_ARG, "pw_group: null pointer argument");
+  return pw::launch_group(bits, nq, hkv, n_pages, window, max_group, n_groups, group_qids,
+                          group_size, stream);
+}
+
+pw_status pw_union_tables(const uint64_t* bits, int n_rows, int hkv, int n_pages,
+                          const int32_t* group_rows, const int32_t* group_size, int n_groups,
+                          int group_width, int k_max, int32_t* union_off, int32_t* union_pages,
+                          uint8_t* union_qmask, int64_t capacity, hipStream_t stream) {
+  pw::g_err[0] = 0;
+  if (n_rows < 0 || hkv < 1 || n_pages < 1 || n_groups < 0 || k_max < 0)
+    return fail(PW_ERR_ARG, "pw_union_tables: bad sizes n_rows=%d hkv=%d n_pages=%d n_groups=%d k_max=%d",
+                n_rows, hkv, n_pages, n_groups, k_max);
+  if (group_width < 1 || group_width > 64)
+    return fail(PW_ERR_UNSUPPORTED, "pw_union_tables: group_width=%d not in 1..64", group_width);
+  if (union_qmask && group_width > 8)
+    return fail(PW_ERR_UNSUPPORTED, "pw_union_tables: member masks need group_width <= 8 (got %d)",
+                group_width);
+  if (n_pages > 65536)
+    return fail(PW_ERR_UNSUPPORTED, "pw_union_tables: n_pages=%d > 65536", n_pages);
+  const int64_t n_tables = (int64_t)hkv * n_groups;
+  if (n_tables >= INT32_MAX)
+    return fail(PW_ERR_UNSUPPORTED, "pw_union_tables: too many tables");
+  const int64_t need = pw_union_capacity((int)n_tables, group_width, k_max, n_pages);
+  if (capacity < need)
+    return fail(PW_ERR_CAPACITY, "pw_union_tables: capacity %lld < required %lld",
+                (long long)capacity, (long long)need);
+  if (capacity > INT32_MAX)
+    return fail(PW_ERR_UNSUPPORTED, "pw_union_tables: capacity %lld exceeds int32 offsets",
+                (long long)capacity);
+  if (!union_off) return fail(PW_ERR_ARG, "pw_union_tables: null union_off");
+  if (n_tables > 0 && (!bits || !group_rows || (need > 0 && !union_pages)))
+    return fail(PW_ERR_ARG, "pw_union_tables: null pointer argument");
+  return pw::launch_union_tables(bits, n_rows, hkv, n_pages, group_rows, group_size, n_groups,
+                                 group_width, union_off, union_pages, union_qmask, capacity,
+                                 stream);
+}
+
+pw_status pw_sparse_prefill(const void* q, int nq, int hq, int hkv, int d, const void* k_cache,
+                            const void* v_cache, int kv_dtype, const float* k_scale,
+                            const float* v_scale, int page_size, int n_pages, int64_t stride_head,
+                            int64_t stride_page, const int32_t* q_pos, int kv_len, float sm_scale,
+                            const int32_t* group_qids, const int32_t* group_size, int n_groups,
+                            int max_group, int shared_table, const int32_t* union_off,
+                            const int32_t* union_pages, const uint8_t* union_qmask,
+                            int64_t capacity, void* out, float* lse, hipStream_t stream) {
+  pw::g_err[0] = 0;
+  if (nq < 0 || hq < 1 || hkv < 1 || n_pages < 1 || n_groups < 0 || kv_len < 0 || capacity < 0)
+    return fail(PW_ERR_ARG, "pw_sparse_prefill: bad sizes nq=%d hq=%d hkv=%d n_pages=%d n_groups=%d kv_len=%d",
+                nq, hq, hkv, n_pages, n_groups, kv_len);
+  if (hq % hkv) return fail(PW_ERR_ARG, "pw_sparse_prefill: hq=%d not a multiple of hkv=%d", hq, hkv);
+  if (d != 64 && d != 128) return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: d=%d (64 or 128)", d);
+  if (page_size != 64 && page_size != 128)
+    return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: page_size=%d (64 or 128)", page_size);
+  if (max_group < 1 || max_group > 8)
+    return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: max_group=%d not in 1..8", max_group);
+  const int G = hq / hkv;
+  if (G * max_group > 64)
+    return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: (hq/hkv)*max_group=%d > 64", G * max_group);
+  if (kv_dtype != PW_KV_BF16 && kv_dtype != PW_KV_FP8_E4M3)
+    return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: kv_dtype=%d", kv_dtype);
+  if (shared_table != 0 && shared_table != 1)
+    return fail(PW_ERR_ARG, "pw_sparse_prefill: shared_table=%d (0 or 1)", shared_table);
+  const int esz = kv_dtype == PW_KV_FP8_E4M3 ? 1 : 2;
+  if (stride_page < (int64_t)page_size * d || stride_head < 0)
+    return fail(PW_ERR_ARG, "pw_sparse_prefill: stride_page=%lld < page_size*d or stride_head < 0",
+                (long long)stride_page);
+  if ((stride_page * esz) % 16 || (stride_head * esz) % 16)
+    return fail(PW_ERR_ARG, "pw_sparse_prefill: strides must be multiples of 16 bytes");
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) % 16)
+    return fail(PW_ERR_ARG, "pw_sparse_prefill: q, caches and out must be 16-byte aligned");
+  if (!group_qids && n_groups * (int64_t)max_group < nq)
+    return fail(PW_ERR_ARG, "pw_sparse_prefill: consecutive groups need n_groups*max_group >= nq");
+  if ((int64_t)hkv * n_groups >= INT32_MAX / 8)
+    return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: too many work items");
+  if (!(sm_scale > 0.f) || sm_scale != sm_scale)
+    return fail(PW_ERR_ARG, "pw_sparse_prefill: sm_scale must be positive");
+  const bool work = nq > 0 && n_groups > 0;
+  if (work) {
+    if (!q || !k_cache || !v_cache || !q_pos || !union_off || !out)
+      return fail(PW_ERR_ARG, "pw_sparse_prefill: null required pointer");
+    if (group_qids && !group_size)
+      return fail(PW_ERR_ARG, "pw_sparse_prefill: group_size is required with group_qids");
+    if (kv_dtype == PW_KV_FP8_E4M3 && (!k_scale || !v_scale))
+      return fail(PW_ERR_ARG, "pw_sparse_prefill: fp8 KV needs k_scale and v_scale");
+    if (capacity > 0 && !union_pages) return fail(PW_ERR_ARG, "pw_sparse_prefill: null union_pages");
+  }
+  if (!work) return PW_OK;
+  pw::AttnArgs a{q, nq, hq, hkv, d, k_cache, v_cache, kv_dtype, k_scale, v_scale, page_size,
+                 n_pages, stride_head, stride_page, q_pos, kv_len, sm_scale, group_qids, group_size,
+                 n_groups, max_group, shared_table, union_off, union_pages, union_qmask, capacity,
+                 out, lse};
+  return pw::launch_sparse_prefill(a, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Internal declarations shared by the host API and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pw.h"
+
+namespace pw {
+
+// Records a formatted error message for pw_last_error() and returns `status`.
+pw_status fail(pw_status status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// Turns the result of the last launch into a status.
+pw_status check_launch(const char* what);
+
+// ---- launchers (validated arguments only) --------------------------------------------
+pw_status launch_page_bitsets(const int32_t* topk, int n_rows, int hkv, int k, int n_pages,
+                              uint64_t* bits, int32_t* bad_id_count, hipStream_t stream);
+
+pw_status launch_group(const uint64_t* bits, int nq, int hkv, int n_pages, int window,
+                       int max_group, int n_groups, int32_t* group_qids, int32_t* group_size,
+                       hipStream_t stream);
+
+pw_status launch_union_tables(const uint64_t* bits, int n_rows, int hkv, int n_pages,
+                              const int32_t* group_rows, const int32_t* group_size, int n_groups,
+                              int group_width, int32_t* union_off, int32_t* union_pages,
+                              uint8_t* union_qmask, int64_t capacity, hipStream_t stream);
+
+struct AttnArgs {
+  const void* q;
+  int nq, hq, hkv, d;
+  const void* k_cache;
+  const void* v_cache;
+  int kv_dtype;
+  const float* k_scale;
+  const float* v_scale;
+  int page_size, n_pages;
+  int64_t stride_head, stride_page;
+  const int32_t* q_pos;
+  int kv_len;
+  float sm_scale;
+  const int32_t* group_qids;
+  const int32_t* group_size;
+  int n_groups, max_group, shared_table;
+  const int32_t* union_off;
+  const int32_t* union_pages;
+  const uint8_t* union_qmask;
+  int64_t capacity;
+  void* out;
+  float* lse;
+};
+
+pw_status launch_sparse_prefill(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace pw

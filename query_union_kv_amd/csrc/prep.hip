@@ -1,0 +1,368 @@
+// Preparation kernels for query-union execution on gfx950 (wave64):
+//   page bitsets   -- wavefront ballots over LDS page flags
+//   grouping       -- bounded greedy affinity search, one workgroup per (KV head, window)
+//   union tables   -- OR + popcount, prefix sum, compaction into ascending page lists
+//
+// Method: "PageWeaver: KV-Guided Query Unions for Sparse Attention" (abstract,
+// Figs. 1-2): fixed TopK pages per query, a bounded GPU search over
+// selected-page affinity that returns query IDs, and per-group page unions
+// whose members keep their own supports.  "CompactAttention" (summary,
+// "Approach"): unions across Q-blocks and heads of a KV group give one block
+// table per KV group; the union kernels build both.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace pw {
+namespace {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+// Exclusive prefix sum across the wave (lane order).
+__device__ __forceinline__ int wave_excl_scan(int v, int lane) {
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  return x - v;
+}
+// Makes this wave's earlier LDS writes visible to its later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------------------
+// (1) page bitsets.  Each wave owns an LDS flag array of `words*64` bytes, one byte per
+// page.  For a row, lanes holding valid IDs set their page's flag; then for every 64-page
+// word the wave reads 64 consecutive flags (lane l <-> page 64w + l) and one ballot is the
+// word.  Flags are cleared as they are read, so the array is zero again for the next row.
+// Duplicate IDs write the same flag; negative IDs are skipped; IDs >= n_pages are counted.
+__global__ void k_page_bitsets(const int32_t* __restrict__ topk, int n_rows, int hkv, int k,
+                               int n_pages, int words, uint64_t* __restrict__ bits,
+                               int32_t* __restrict__ bad_id_count) {
+  extern __shared__ uint8_t flags_all[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int waves = blockDim.x / kWave;
+  uint8_t* flags = flags_all + (size_t)wave * words * kWave;
+  for (int i = lane; i < words * kWave; i += kWave) flags[i] = 0;
+  wave_lds_sync();
+
+  const int64_t total = (int64_t)n_rows * hkv;
+  int bad = 0;
+  for (int64_t item = (int64_t)blockIdx.x * waves + wave; item < total;
+       item += (int64_t)gridDim.x * waves) {
+    const int g = (int)(item / n_rows);
+    const int r = (int)(item - (int64_t)g * n_rows);
+    const int32_t* ids = topk + ((int64_t)r * hkv + g) * k;
+    for (int j = lane; j < k; j += kWave) {
+      const int id = ids[j];
+      if (id >= n_pages) ++bad;
+      else if (id >= 0) flags[id] = 1;
+    }
+    wave_lds_sync();
+    uint64_t* dst = bits + item * words;   // item = g * n_rows + r
+    uint64_t mine = 0;
+    for (int w = 0; w < words; ++w) {
+      const bool f = flags[w * kWave + lane] != 0;
+      const uint64_t word = __ballot(f);
+      flags[w * kWave + lane] = 0;
+      if (lane == (w & (kWave - 1))) mine = word;
+      if ((w & (kWave - 1)) == kWave - 1 || w == words - 1) {
+        const int base = w & ~(kWave - 1);
+        if (lane <= w - base) dst[base + lane] = mine;
+      }
+    }
+    wave_lds_sync();
+  }
+  bad = wave_sum(bad);
+  if (bad_id_count != nullptr && lane == 0 && bad > 0) atomicAdd(bad_id_count, bad);
+}
+
+// ---------------------------------------------------------------------------------------
+// (2) bounded greedy affinity grouping.  One workgroup per (window, KV head); thread c is
+// candidate query start + c and keeps its bitset in registers (MAXW words).  The group
+// union U lives in LDS.  Every pick is a workgroup argmax over the key
+// (overlap << 11) | (2047 - c), so equal overlaps resolve to the lower query ID.
+template <int MAXW>
+__global__ void k_group(const uint64_t* __restrict__ bits, int nq, int words, int window,
+                        int max_group, int n_groups, int32_t* __restrict__ group_qids,
+                        int32_t* __restrict__ group_size) {
+  __shared__ uint64_t U[MAXW];
+  __shared__ int red[16];
+  const int g = blockIdx.y;
+  const int start = blockIdx.x * window;
+  const int len = min(window, nq - start);
+  const int c = threadIdx.x;
+  const int lane = c & (kWave - 1), wave = c / kWave;
+  const int nwaves = blockDim.x / kWave;
+  const bool valid = c < len;
+
+  uint64_t mine[MAXW];
+  const uint64_t* row = bits + ((int64_t)g * nq + start + c) * words;
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w) mine[w] = (valid && w < words) ? row[w] : 0ull;
+
+  auto block_max = [&](int v) -> int {
+    v = wave_max(v);
+    if (nwaves > 1) {
+      if (lane == 0) red[wave] = v;
+      __syncthreads();
+      int r = red[0];
+      for (int i = 1; i < nwaves; ++i) r = max(r, red[i]);
+      __syncthreads();
+      v = r;
+    }
+    return v;
+  };
+
+  bool is_free = valid;
+  int remaining = len;
+  int gi = 0;
+  const int64_t gbase = (int64_t)g * n_groups + (int64_t)blockIdx.x * (window / max_group);
+  while (remaining > 0) {
+    // seed: the lowest ungrouped ID (max of 2047 - c over free lanes)
+    const int seed = 2047 - block_max(is_free ? 2047 - c : -1);
+    if (c == seed) {
+      is_free = false;
+#pragma unroll
+      for (int w = 0; w < MAXW; ++w) if (w < words) U[w] = mine[w];
+    }
+    __syncthreads();
+    int members[8];
+    members[0] = seed;
+    int cnt = 1;
+    --remaining;
+    while (cnt < max_group && remaining > 0) {
+      int score = 0;
+#pragma unroll
+      for (int w = 0; w < MAXW; ++w)
+        if (w < words) score += __popcll(mine[w] & U[w]);
+      const int best = block_max(is_free ? ((score << 11) | (2047 - c)) : -1);
+      const int pick = 2047 - (best & 2047);
+      __syncthreads();                       // every lane has read U before it changes
+      if (c == pick) {
+        is_free = false;
+#pragma unroll
+        for (int w = 0; w < MAXW; ++w) if (w < words) U[w] |= mine[w];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 1; j < 8; ++j) if (j == cnt) members[j] = pick;
+      ++cnt;
+      --remaining;
+    }
+    if (c < max_group) {
+      int v = -1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) if (j == c && j < cnt) v = start + members[j];
+      group_qids[(gbase + gi) * max_group + c] = v;
+    }
+    if (c == 0) group_size[gbase + gi] = cnt;
+    ++gi;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// (3) union tables.  Table e = g * n_groups + j; one wave per table.
+__device__ __forceinline__ int member_count(const int32_t* group_size, int e, int group_width) {
+  return group_size ? min(max(group_size[e], 0), group_width) : group_width;
+}
+
+__global__ void k_union_count(const uint64_t* __restrict__ bits, int n_rows, int words,
+                              const int32_t* __restrict__ group_rows,
+                              const int32_t* __restrict__ group_size, int n_groups, int n_tables,
+                              int group_width, int32_t* __restrict__ union_off) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int e = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (e >= n_tables) return;
+  const int g = e / n_groups;
+  const int sz = member_count(group_size, e, group_width);
+  const int32_t* rows = group_rows + (int64_t)e * group_width;
+  int cnt = 0;
+  for (int w = lane; w < words; w += kWave) {
+    uint64_t u = 0;
+    for (int j = 0; j < sz; ++j) {
+      const int r = rows[j];
+      if (r >= 0 && r < n_rows) u |= bits[((int64_t)g * n_rows + r) * words + w];
+    }
+    cnt += __popcll(u);
+  }
+  cnt = wave_sum(cnt);
+  if (lane == 0) union_off[e + 1] = cnt;
+}
+
+// In-place inclusive scan of union_off[1 .. n] by one workgroup of 1024 threads, so that
+// union_off becomes the exclusive prefix sum of the table sizes.
+__global__ void k_union_scan(int32_t* __restrict__ union_off, int n) {
+  __shared__ int wsum[16];
+  __shared__ int carry_s;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  if (t == 0) {
+    carry_s = 0;
+    union_off[0] = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < n; base += 1024) {
+    const int i = base + t;
+    const int v = i < n ? union_off[i + 1] : 0;
+    const int ex = wave_excl_scan(v, lane);
+    if (lane == kWave - 1) wsum[wave] = ex + v;
+    __syncthreads();
+    int before = carry_s;
+    for (int k = 0; k < wave; ++k) before += wsum[k];
+    if (i < n) union_off[i + 1] = before + ex + v;
+    __syncthreads();
+    if (t == 1023) carry_s = before + ex + v;
+    __syncthreads();
+  }
+}
+
+template <bool QMASK>
+__global__ void k_union_emit(const uint64_t* __restrict__ bits, int n_rows, int words,
+                             const int32_t* __restrict__ group_rows,
+                             const int32_t* __restrict__ group_size, int n_groups, int n_tables,
+                             int group_width, const int32_t* __restrict__ union_off,
+                             int32_t* __restrict__ union_pages, uint8_t* __restrict__ union_qmask,
+                             int64_t capacity) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int e = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (e >= n_tables) return;
+  const int g = e / n_groups;
+  const int sz = member_count(group_size, e, group_width);
+  const int32_t* rows = group_rows + (int64_t)e * group_width;
+  int64_t pos = union_off[e];
+  for (int w0 = 0; w0 < words; w0 += kWave) {
+    const int w = w0 + lane;
+    uint64_t u = 0;
+    uint64_t mw[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mw[j] = 0;
+    if (w < words) {
+      for (int j = 0; j < sz; ++j) {
+        const int r = rows[j];
+        if (r < 0 || r >= n_rows) continue;
+        const uint64_t b = bits[((int64_t)g * n_rows + r) * words + w];
+        u |= b;
+        if (QMASK) {
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) if (jj == j) mw[jj] = b;
+        }
+      }
+    }
+    const int pc = __popcll(u);
+    int64_t p = pos + wave_excl_scan(pc, lane);
+    const int chunk_total = wave_sum(pc);
+    while (u) {
+      const int b = __ffsll((unsigned long long)u) - 1;
+      u &= u - 1;
+      if (p < capacity) {
+        union_pages[p] = w * 64 + b;
+        if (QMASK) {
+          int qm = 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) qm |= (int)((mw[j] >> b) & 1ull) << j;
+          union_qmask[p] = (uint8_t)qm;
+        }
+      }
+      ++p;
+    }
+    pos += chunk_total;
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------
+pw_status launch_page_bitsets(const int32_t* topk, int n_rows, int hkv, int k, int n_pages,
+                              uint64_t* bits, int32_t* bad_id_count, hipStream_t stream) {
+  const int words = (n_pages + 63) / 64;
+  const int64_t total = (int64_t)n_rows * hkv;
+  if (total == 0) return PW_OK;
+  const int per_wave = words * kWave;
+  const int waves = std::max(1, std::min(4, 65536 / per_wave));
+  const int64_t want = (total + waves - 1) / waves;
+  const int blocks = (int)std::min<int64_t>(want, 8192);
+  hipLaunchKernelGGL(k_page_bitsets, dim3(blocks), dim3(waves * kWave),
+                     (size_t)waves * per_wave, stream, topk, n_rows, hkv, k, n_pages, words, bits,
+                     bad_id_count);
+  return check_launch("page_bitsets");
+}
+
+pw_status launch_group(const uint64_t* bits, int nq, int hkv, int n_pages, int window,
+                       int max_group, int n_groups, int32_t* group_qids, int32_t* group_size,
+                       hipStream_t stream) {
+  if (nq == 0) return PW_OK;
+  const int words = (n_pages + 63) / 64;
+  const int n_windows = (nq + window - 1) / window;
+  const int threads = ((std::min(window, nq) + kWave - 1) / kWave) * kWave;
+  dim3 grid(n_windows, hkv), block(threads);
+#define PW_GROUP_CASE(W)                                                                     \
+  if (words <= W) {                                                                          \
+    hipLaunchKernelGGL(k_group<W>, grid, block, 0, stream, bits, nq, words, window, max_group, \
+                       n_groups, group_qids, group_size);                                    \
+    return check_launch("group");                                                            \
+  }
+  PW_GROUP_CASE(1)
+  PW_GROUP_CASE(2)
+  PW_GROUP_CASE(4)
+  PW_GROUP_CASE(8)
+  PW_GROUP_CASE(16)
+  PW_GROUP_CASE(32)
+  PW_GROUP_CASE(64)
+#undef PW_GROUP_CASE
+  return fail(PW_ERR_UNSUPPORTED, "pw_group: n_pages=%d needs %d words > 64", n_pages, words);
+}
+
+pw_status launch_union_tables(const uint64_t* bits, int n_rows, int hkv, int n_pages,
+                              const int32_t* group_rows, const int32_t* group_size, int n_groups,
+                              int group_width, int32_t* union_off, int32_t* union_pages,
+                              uint8_t* union_qmask, int64_t capacity, hipStream_t stream) {
+  const int words = (n_pages + 63) / 64;
+  const int n_tables = hkv * n_groups;
+  if (n_tables == 0) {   // only union_off[0] = 0
+    hipLaunchKernelGGL(k_union_scan, dim3(1), dim3(1024), 0, stream, union_off, 0);
+    return check_launch("union_scan");
+  }
+  const int wpb = 4;
+  const int blocks = (n_tables + wpb - 1) / wpb;
+  hipLaunchKernelGGL(k_union_count, dim3(blocks), dim3(wpb * kWave), 0, stream, bits, n_rows,
+                     words, group_rows, group_size, n_groups, n_tables, group_width, union_off);
+  pw_status st = check_launch("union_count");
+  if (st != PW_OK) return st;
+  hipLaunchKernelGGL(k_union_scan, dim3(1), dim3(1024), 0, stream, union_off, n_tables);
+  st = check_launch("union_scan");
+  if (st != PW_OK) return st;
+  if (union_qmask)
+    hipLaunchKernelGGL(k_union_emit<true>, dim3(blocks), dim3(wpb * kWave), 0, stream, bits,
+                       n_rows, words, group_rows, group_size, n_groups, n_tables, group_width,
+                       union_off, union_pages, union_qmask, capacity);
+  else
+    hipLaunchKernelGGL(k_union_emit<false>, dim3(blocks), dim3(wpb * kWave), 0, stream, bits,
+                       n_rows, words, group_rows, group_size, n_groups, n_tables, group_width,
+                       union_off, union_pages, union_qmask, capacity);
+  return check_launch("union_emit");
+}
+
+}  // namespace pw

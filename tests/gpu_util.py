@@ -1,0 +1,106 @@
+"""Shared pieces of the GPU parity tests: moving a workload to the device, running
+the HIP path through the C ABI, and the oracle's view of the same call."""
+import math
+
+import numpy as np
+import torch
+
+import query_union_kv_amd as pw
+from oracle import attention, prep
+
+TOL = {"bf16": dict(max_abs=2e-2, mean_abs=2e-3), "fp8": dict(max_abs=6e-2, mean_abs=None)}
+
+
+def device_inputs(w, dev="cuda"):
+    c = w.cfg
+    d = {}
+    d["q"] = torch.from_numpy(w.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    if c.kv_dtype == "bf16":
+        d["k"] = torch.from_numpy(w.k.view(np.int16)).view(torch.bfloat16).to(dev)
+        d["v"] = torch.from_numpy(w.v.view(np.int16)).view(torch.bfloat16).to(dev)
+        d["k_scale"] = d["v_scale"] = None
+    else:
+        d["k"] = torch.from_numpy(w.k).to(dev)
+        d["v"] = torch.from_numpy(w.v).to(dev)
+        d["k_scale"] = torch.from_numpy(w.k_scale).to(dev)
+        d["v_scale"] = torch.from_numpy(w.v_scale).to(dev)
+    d["q_pos"] = torch.from_numpy(np.ascontiguousarray(w.q_pos, dtype=np.int32)).to(dev)
+    ids = w.topk if w.topk is not None else w.mask_rows
+    d["ids"] = torch.from_numpy(np.ascontiguousarray(ids)).to(dev)
+    return d
+
+
+def make_plan(w, grouping="affinity", window=None, max_group=None, dev="cuda"):
+    c = w.cfg
+    ids = w.topk if w.topk is not None else w.mask_rows
+    mode = "topk" if w.topk is not None else "block_union"
+    return pw.SparsePrefill(nq=c.nq, hq=c.hq, hkv=c.hkv, d=c.d, n_pages=c.n_pages, page_size=c.ps,
+                            kv_len=c.kv_len, k=ids.shape[2], window=window or c.window,
+                            max_group=max_group or c.max_group, mode=mode, grouping=grouping,
+                            n_rows=ids.shape[0] if mode == "block_union" else 0, device=dev)
+
+
+def run_gpu(w, grouping="affinity", window=None, max_group=None, with_lse=True):
+    d = device_inputs(w)
+    plan = make_plan(w, grouping, window, max_group)
+    out = torch.full_like(d["q"], float("nan"))
+    lse = torch.full(d["q"].shape[:2], float("nan"), dtype=torch.float32, device="cuda") if with_lse else None
+    plan(d["ids"], d["q"], d["k"], d["v"], d["q_pos"], out, d["k_scale"], d["v_scale"], lse)
+    torch.cuda.synchronize()
+    res = {"out": out.float().cpu().numpy(), "bits": plan.bits.cpu().numpy().view(np.uint64),
+           "union_off": plan.union_off.cpu().numpy(), "bad_ids": int(plan.bad_ids.item())}
+    total = int(res["union_off"][-1])
+    res["union_pages"] = plan.union_pages[:total].cpu().numpy()
+    if plan.union_qmask is not None:
+        res["union_qmask"] = plan.union_qmask[:total].cpu().numpy()
+        res["group_qids"] = plan.group_qids.cpu().numpy()
+        res["group_size"] = plan.group_size.cpu().numpy()
+    if with_lse:
+        res["lse"] = lse.cpu().numpy()
+    return res, plan
+
+
+def oracle_tables(w, grouping="affinity", window=None, max_group=None):
+    """Bitsets, groups and union tables exactly as the oracle defines them."""
+    c = w.cfg
+    window = window or c.window
+    max_group = max_group or c.max_group
+    if w.topk is not None:
+        bits = prep.page_bitsets(w.topk, c.n_pages)
+        if grouping == "affinity":
+            groups = [prep.group_affinity(b, window, max_group) for b in bits]
+        else:
+            groups = [prep.group_original(c.nq, max_group) for _ in bits]
+        qids, size = prep.groups_to_arrays(groups, max_group)
+        off, pages, qmask = prep.union_tables(bits, groups)
+        return {"bits": prep.bits_to_words(bits, c.n_pages), "group_qids": qids, "group_size": size,
+                "union_off": off, "union_pages": pages, "union_qmask": qmask, "groups": groups,
+                "S": prep.supports(w.topk, c.n_pages), "stats": prep.union_stats(bits, groups)}
+    bits = prep.page_bitsets(w.mask_rows, c.n_pages)
+    n_rows = w.mask_rows.shape[0]
+    off, pages, _ = prep.union_tables(bits, [[list(range(n_rows))] for _ in bits], with_qmask=False)
+    tables = prep.block_tables(w.mask_rows, c.n_pages)
+    return {"bits": prep.bits_to_words(bits, c.n_pages), "union_off": off, "union_pages": pages,
+            "tables": tables, "S": attention.shared_supports(tables, c.nq)}
+
+
+def oracle_attention(w, S, queries=None):
+    c = w.cfg
+    return attention.route_a(w.q, w.k, w.v, w.k_scale, w.v_scale, c.kv_dtype, S, w.q_pos,
+                             c.kv_len, c.ps, 1.0 / math.sqrt(c.d), queries)
+
+
+def check_close(got, ref, kv_dtype, what=""):
+    err = np.abs(got.astype(np.float64) - ref)
+    tol = TOL[kv_dtype]
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    assert err.max() <= tol["max_abs"], f"{what}: max_abs {err.max():.4g} > {tol['max_abs']}"
+    if tol["mean_abs"] is not None:
+        assert err.mean() <= tol["mean_abs"], f"{what}: mean_abs {err.mean():.4g} > {tol['mean_abs']}"
+    return float(err.max()), float(err.mean()), attention.nrms(got, ref)
+
+
+def check_lse(got, ref, what=""):
+    fin = np.isfinite(ref)
+    assert (np.isneginf(got) == ~fin).all(), f"{what}: lse -inf pattern differs"
+    assert np.abs(got[fin] - ref[fin]).max(initial=0) <= 2e-3, f"{what}: lse differs"

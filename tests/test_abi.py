@@ -1,0 +1,124 @@
+"""The C-ABI library: it loads, exports every entry point include/pw.h declares, and
+rejects bad arguments on the host before any device work (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import query_union_kv_amd as pw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pw.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pw_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert {"pw_page_bitsets", "pw_group", "pw_union_tables", "pw_sparse_prefill"} <= set(names)
+    L = ctypes.CDLL(pw.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_host_helpers():
+    assert pw.pw_version()
+    assert pw.pw_words(1) == 1 and pw.pw_words(64) == 1 and pw.pw_words(65) == 2
+    assert pw.pw_num_groups(256, 64, 8) == 32
+    assert pw.pw_num_groups(70, 64, 8) == 9
+    assert pw.pw_num_groups(75, 64, 8) == 10
+    assert pw.pw_num_groups(0, 64, 8) == 0
+    assert pw.pw_num_groups(10, 0, 8) == -1
+    assert pw.pw_union_capacity(4096, 8, 16, 1024) == 4096 * 128
+    assert pw.pw_union_capacity(8, 32, 205, 1024) == 8 * 1024
+
+
+L = pw.lib()
+NULL = None
+
+
+def _err(status):
+    return status, L.pw_last_error().decode()
+
+
+@pytest.mark.parametrize("args,code", [
+    ((NULL, 4, 1, 0, 16, NULL, NULL, NULL), -1),       # k = 0
+    ((NULL, 4, 0, 4, 16, NULL, NULL, NULL), -1),       # hkv = 0
+    ((NULL, 4, 1, 4, 0, NULL, NULL, NULL), -1),        # n_pages = 0
+    ((NULL, 4, 1, 5000, 16, NULL, NULL, NULL), -2),    # k too large
+    ((NULL, 4, 1, 4, 70000, NULL, NULL, NULL), -2),    # too many pages
+    ((NULL, 4, 1, 4, 16, NULL, NULL, NULL), -1),       # null pointers
+])
+def test_bitsets_validation(args, code):
+    st, msg = _err(L.pw_page_bitsets(*args))
+    assert st == code and msg.startswith("pw_page_bitsets")
+
+
+def test_bitsets_empty_is_ok():
+    assert L.pw_page_bitsets(NULL, 0, 1, 4, 16, NULL, NULL, NULL) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((NULL, 64, 1, 16, 64, 9, NULL, NULL, NULL), -2),   # max_group 9
+    ((NULL, 64, 1, 16, 60, 8, NULL, NULL, NULL), -1),   # window % max_group
+    ((NULL, 64, 1, 16, 2048, 8, NULL, NULL, NULL), -2), # window > 1024
+    ((NULL, 64, 1, 5000, 64, 8, NULL, NULL, NULL), -2), # n_pages > 4096
+    ((NULL, 64, 1, 16, 64, 8, NULL, NULL, NULL), -1),   # null pointers
+    ((NULL, -1, 1, 16, 64, 8, NULL, NULL, NULL), -1),   # nq < 0
+])
+def test_group_validation(args, code):
+    st, msg = _err(L.pw_group(*args))
+    assert st == code and msg.startswith("pw_group")
+
+
+@pytest.mark.parametrize("args,code", [
+    # bits, n_rows, hkv, n_pages, rows, size, n_groups, width, k_max, off, pages, qmask, cap, stream
+    ((NULL, 8, 1, 16, NULL, NULL, 1, 0, 4, NULL, NULL, NULL, 64, NULL), -2),    # width 0
+    ((NULL, 8, 1, 16, NULL, NULL, 1, 65, 4, NULL, NULL, NULL, 64, NULL), -2),   # width 65
+    ((NULL, 8, 1, 16, NULL, NULL, 1, 16, 4, NULL, NULL, 1, 64, NULL), -2),      # qmask needs width <= 8
+    ((NULL, 8, 1, 16, NULL, NULL, 2, 8, 4, NULL, NULL, NULL, 31, NULL), -3),    # capacity < 2*16
+    ((NULL, 8, 1, 16, NULL, NULL, 2, 8, 4, NULL, NULL, NULL, 32, NULL), -1),    # null union_off
+])
+def test_union_validation(args, code):
+    st, msg = _err(L.pw_union_tables(*args))
+    assert st == code and msg.startswith("pw_union_tables")
+
+
+def _attn(**kw):
+    a = dict(q=NULL, nq=8, hq=4, hkv=1, d=128, k=NULL, v=NULL, kv_dtype=0, ks=NULL, vs=NULL, ps=64,
+             n_pages=4, sh=4 * 64 * 128, sp=64 * 128, q_pos=NULL, kv_len=256, sm=0.088,
+             gq=NULL, gs=NULL, n_groups=1, mg=8, shared=0, off=NULL, pages=NULL, qmask=NULL,
+             cap=4, out=NULL, lse=NULL, stream=NULL)
+    a.update(kw)
+    return _err(L.pw_sparse_prefill(*a.values()))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), -2), (dict(ps=32), -2), (dict(hq=6, hkv=4), -1), (dict(mg=9), -2),
+    (dict(hq=16, mg=8), -2),                       # G * max_group = 128 > 64
+    (dict(kv_dtype=2), -2), (dict(shared=2), -1), (dict(sp=100), -1),
+    (dict(n_groups=0, nq=9), -1),                  # consecutive groups must cover nq
+    (dict(sm=0.0), -1), (dict(nq=-1), -1),
+    (dict(), -1),                                  # null required pointers
+])
+def test_attention_validation(kw, code):
+    st, msg = _attn(**kw)
+    assert st == code and msg.startswith("pw_sparse_prefill"), msg
+
+
+def test_attention_nothing_to_do_is_ok():
+    assert _attn(nq=0)[0] == 0
+    assert _attn(n_groups=0, nq=0)[0] == 0
+
+
+def test_binding_rejects_host_tensors():
+    topk = torch.zeros((4, 1, 2), dtype=torch.int32)
+    bits = torch.zeros((1, 4, 1), dtype=torch.int64)
+    with pytest.raises(ValueError):
+        pw.pw_page_bitsets(topk, 16, bits)

@@ -1,0 +1,145 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Integer outputs (bitsets, groups, union tables, member masks) must match bit for
+bit; attention outputs must be within max-abs 2e-2 and mean-abs 2e-3 for bf16 KV
+and max-abs 6e-2 for fp8 KV.  Full-size workloads compare every integer table
+and a sample of attention rows (the oracle computes rows one by one); small
+shapes compare everything.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import (check_close, check_lse, oracle_attention, oracle_tables, run_gpu)
+from helpers import add_padding_and_duplicates
+from workloads import CONFIGS, make_workload
+from workloads.configs import Config
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(nq, n=40, seed=0):
+    rng = np.random.default_rng(seed)
+    edge = [0, 1, 7, 8, 63, 64, nq - 9, nq - 8, nq - 2, nq - 1]
+    s = sorted(set([i for i in edge if 0 <= i < nq] + list(rng.choice(nq, size=min(n, nq), replace=False))))
+    return s
+
+
+def _compare_tables(res, ref, has_groups=True):
+    assert np.array_equal(res["bits"], ref["bits"]), "bitsets differ"
+    if has_groups:
+        assert np.array_equal(res["group_size"], ref["group_size"]), "group sizes differ"
+        assert np.array_equal(res["group_qids"], ref["group_qids"]), "group ids differ"
+    assert np.array_equal(res["union_off"], ref["union_off"]), "union offsets differ"
+    assert np.array_equal(res["union_pages"], ref["union_pages"]), "union pages differ"
+    if has_groups:
+        assert np.array_equal(res["union_qmask"], ref["union_qmask"]), "member masks differ"
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_workload_parity(name):
+    cfg = CONFIGS[name]
+    print(f"[parity] {name}", flush=True)
+    w = make_workload(cfg)
+    res, _ = run_gpu(w)
+    ref = oracle_tables(w)
+    _compare_tables(res, ref, has_groups=w.topk is not None)
+    assert res["bad_ids"] == 0
+    queries = list(range(cfg.nq)) if cfg.nq * cfg.hkv <= 4096 else _sample(cfg.nq)
+    O, L = oracle_attention(w, ref["S"], queries)
+    mx, mean, nrms = check_close(res["out"][queries], O, cfg.kv_dtype, name)
+    check_lse(res["lse"][queries], L, name)
+    print(f"[parity] {name}: rows={len(queries)} max_abs={mx:.3e} mean_abs={mean:.3e} nrms={nrms:.3f}%",
+          flush=True)
+
+
+def _small(**kw):
+    base = dict(name="small", hq=4, hkv=1, d=128, ps=64, kv_len=1024, nq=65, kv_dtype="bf16",
+                support="uniform", k=4, forced=False, window=64, max_group=8, seed=31)
+    base.update(kw)
+    return Config(**base)
+
+
+SMALL = [
+    dict(nq=1), dict(nq=7), dict(nq=8), dict(nq=9), dict(nq=63), dict(nq=64), dict(nq=65),
+    dict(k=1), dict(k=16, kv_len=2048), dict(k=64, kv_len=8192, nq=130),
+    dict(hq=1, hkv=1), dict(hq=8, hkv=1), dict(hq=16, hkv=2, max_group=4),
+    dict(d=64), dict(ps=128, kv_len=2048), dict(kv_dtype="fp8"), dict(kv_dtype="fp8", d=64),
+    dict(kv_dtype="fp8", hq=8, hkv=1, k=16, kv_len=4096), dict(kv_len=1000, nq=77),
+    dict(window=16, max_group=4), dict(window=128, nq=300, k=8, kv_len=4096),
+    dict(window=1024, nq=1100, k=6, kv_len=2048, hq=2, hkv=2), dict(max_group=1),
+    dict(support="community", k=6, n_comm=4, comm_size=6, forced=True, kv_len=2048, nq=200),
+    dict(hq=12, hkv=4, max_group=5, window=60, nq=100, k=5),
+]
+
+
+@pytest.mark.parametrize("kw", SMALL, ids=[",".join(f"{k}={v}" for k, v in s.items()) for s in SMALL])
+def test_small_shapes(kw):
+    cfg = _small(**kw)
+    print(f"[parity] small {kw}", flush=True)
+    w = make_workload(cfg)
+    w.topk = add_padding_and_duplicates(w.topk, seed=cfg.seed)
+    res, _ = run_gpu(w)
+    ref = oracle_tables(w)
+    _compare_tables(res, ref)
+    O, L = oracle_attention(w, ref["S"])
+    check_close(res["out"], O, cfg.kv_dtype, str(kw))
+    check_lse(res["lse"], L, str(kw))
+
+
+def test_future_pages_and_empty_supports():
+    cfg = _small(nq=200, kv_len=1024, k=3, hq=8, hkv=2)   # queries on pages 12..15
+    w = make_workload(cfg)
+    n_pages = cfg.n_pages
+    w.topk[:5] = -1                                  # empty supports: O = 0, lse = -inf
+    w.topk[5:10, :, 0] = n_pages - 1                 # page 15 lies wholly in these queries' future
+    w.topk[10:15, :, :] = n_pages - 1                # only future pages
+    res, _ = run_gpu(w)
+    ref = oracle_tables(w)
+    _compare_tables(res, ref)
+    O, L = oracle_attention(w, ref["S"])
+    check_close(res["out"], O, "bf16", "future/empty")
+    check_lse(res["lse"], L, "future/empty")
+    assert (res["out"][:5] == 0).all()
+
+
+def test_out_of_range_ids_are_counted_and_ignored():
+    cfg = _small(nq=16, k=4, hq=4, hkv=2)
+    w = make_workload(cfg)
+    w.topk[3, 1, 2] = cfg.n_pages + 5
+    w.topk[7, 0, 0] = 1 << 20
+    res, _ = run_gpu(w)
+    assert res["bad_ids"] == 2
+    cleaned = w.topk.copy()
+    cleaned[cleaned >= cfg.n_pages] = -1
+    w.topk = cleaned
+    ref = oracle_tables(w)
+    _compare_tables(res, ref)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_grouping_invariance_on_gpu(kv_dtype):
+    cfg = _small(nq=128, k=6, hq=8, hkv=2, kv_len=4096, kv_dtype=kv_dtype,
+                 support="community", n_comm=6, comm_size=10, forced=True)
+    w = make_workload(cfg)
+    outs = {}
+    for name, kw in {"affinity": {}, "original": dict(grouping="original"),
+                     "singletons": dict(max_group=1, window=1)}.items():
+        res, _ = run_gpu(w, **kw)
+        outs[name] = res["out"]
+    ref = oracle_attention(w, oracle_tables(w)["S"])[0]
+    for name, o in outs.items():
+        check_close(o, ref, kv_dtype, name)
+    # masked pages are exact no-ops, so the grouping does not change a single bit
+    assert np.array_equal(outs["affinity"], outs["original"])
+    assert np.array_equal(outs["affinity"], outs["singletons"])
+
+
+def test_run_to_run_determinism():
+    w = make_workload(CONFIGS["c2_gqa_bf16"].scaled(nq=512, kv_len=4096 + 512))
+    a, _ = run_gpu(w)
+    b, _ = run_gpu(w)
+    for k in ("out", "lse", "group_qids", "union_pages", "union_qmask"):
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
