@@ -40,12 +40,26 @@ def parse():
     ap.add_argument("--window", type=int, default=None)
     ap.add_argument("--flush-steps", type=int, default=20,
                     help="extra steps timed one by one after writing 512 MiB (L2/MALL flush)")
-    ap.add_argument("--cpu-queries", type=int, default=256,
+    ap.add_argument("--cpu-queries", type=int, default=4096,
                     help="oracle sample: the first N queries (whole windows), all KV heads")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=None,
                     help="run only this many steps after warmup (for rocprofv3), no extras")
+    ap.add_argument("--calibrate-copy", type=int, default=None, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times (counter calibration)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int) -> None:
+    """A plain copy kernel of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
 
 
 def unique_kv_bytes(union_pages_total: int, cfg) -> int:
@@ -78,6 +92,24 @@ def cpu_baseline(w, n_queries: int) -> dict:
             "cpu": _cpu_model()}
 
 
+def profiled_traffic(workload: str):
+    """HBM-side bytes per attention launch from the committed rocprofv3 summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain-copy calibration), or None if the
+    kernel source changed since the counters were taken."""
+    import hashlib
+    import re
+    src = os.path.join(ROOT, "query_union_kv_amd", "csrc", "attn.hip")
+    summ = os.path.join(ROOT, "profiles", f"k_attn_{workload}.md")
+    if not os.path.exists(summ):
+        return None
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    for line in open(summ):
+        m = re.match(r"traffic_bytes_per_launch\[.*\] = ([0-9.eE+]+)\s+\(attn.hip sha256\[:16\] (\w+)\)", line)
+        if m and m.group(2) == h:
+            return float(m.group(1))
+    return None
+
+
 def _cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -96,6 +128,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import query_union_kv_amd as pw
     from workloads import CONFIGS, make_workload
@@ -245,7 +281,7 @@ def main():
                    "kv_len": cfg.kv_len, "nq": cfg.nq, "topk": cfg.k, "kv_dtype": cfg.kv_dtype,
                    "window": cfg.window, "max_group": cfg.max_group, "seed": w.seed},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "k_attn",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(cfg.name), "kernel": "k_attn",
                      "bytes_per_launch": Bu},
         "extra": extras,
     }
