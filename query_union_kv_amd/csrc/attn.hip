@@ -9,16 +9,23 @@
 // "CompactAttention" (summary, "Approach"): attention reads the paged cache in
 // place, KV-head-major, including one shared block table per KV group.
 //
-// Work item = (KV head g, group j).  Its rows are (member m, head h) pairs,
-// row r = m * G + (h - g*G); wave w of the workgroup owns rows 16w .. 16w+15.
-// Every union page is cut into 64-token tiles.  Per tile:
-//   * all waves stage K and V (64 x D each) into one of two LDS buffers
-//     (global -> registers -> LDS, prefetching the next tile while computing);
-//   * S^T[key][row] = K . Q^T on MFMA (keys are the MFMA rows, so each lane
-//     ends with one query row and 16 of its keys, and row statistics stay in
-//     the lane);
-//   * support mask (member selected the page) + causal mask, online softmax in
-//     the log2 domain;
+// Work item = (KV head g, group j); its rows are (member m, head h) pairs,
+// row r = m * G + (h - g*G).  A workgroup of NW waves owns one item; wave w
+// holds MT row tiles of 16 rows (rows 16*(w*MT + mt) + 0..15), so every K/V
+// fragment read and converted from LDS feeds MT MFMA row tiles.
+//
+// Every union page is cut into 32-token tiles, streamed into an ST-deep LDS
+// ring by direct global->LDS loads (global_load_lds_dwordx4, issued from
+// inline assembly so that the only waits on them are the explicit vmcnt waits
+// below).  Per tile:
+//   * S^T[key][row] = K . Q^T on MFMA: keys are the MFMA rows, so each lane
+//     ends with one query row and 8 of its keys and row statistics stay in
+//     the lane;
+//   * support mask (the member selected the page) + causal mask, online
+//     softmax in the log2 domain; the running maximum used for the
+//     exponentials is only raised when a row's maximum exceeds it by more
+//     than 2^8, so the accumulators are rescaled rarely (exact either way:
+//     numerator and denominator share the reference);
 //   * O^T[d][row] += V^T . P^T on MFMA, V^T read from LDS with the CDNA4
 //     transposing loads (ds_read_b64_tr_b8 / _b16).
 // fp8 (OCP e4m3fn) codes are converted exactly to bf16; the K page scale folds
@@ -26,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -33,9 +41,10 @@ namespace pw {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kTile = 64;          // tokens per tile
+constexpr int kTK = 32;               // tokens per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleMargin = 8.0f;  // log2 units
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -43,8 +52,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define PW_LDS __attribute__((address_space(3)))
+#define PW_CONST __attribute__((address_space(4)))
 
 struct Params {
   const uint16_t* q;
@@ -70,13 +79,16 @@ struct Params {
   float score_scale;       // sm_scale * log2(e)
 };
 
-// XOR swizzle of 16-byte chunks inside an LDS row; keeps the MFMA operand reads and
-// the transposing V reads spread over distinct banks.
+// XOR swizzle of the 16-byte chunks of one LDS token row.  Chosen so that the K
+// operand reads (16 rows per quarter-wave, one chunk each) and the transposing V reads
+// (8 rows x 2 chunks per half-wave) fall on distinct banks.
 template <int CHUNKS>
-__device__ __forceinline__ int swz(int row) {
-  const int f = ((row >> 1) & 1) | ((((row >> 2) ^ (row >> 4)) & 1) << 1) | (((row >> 3) & 1) << 2) |
-                (((row >> 0) & 1) << 3);
-  return f & (CHUNKS - 1);
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CHUNKS >= 16) {
+    return (((r >> 4) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 3)) & (CHUNKS - 1);
+  } else {
+    return (((r >> 1) & 1) | (((r >> 3) & 1) << 1) | ((((r >> 2) ^ (r >> 4)) & 1) << 2)) & (CHUNKS - 1);
+  }
 }
 
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 v) {
@@ -87,27 +99,61 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 v) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-template <int D, bool FP8, int NW>
+// Direct global -> LDS copy of 16 bytes per lane from sbase + voff (sbase wave-uniform,
+// voff per lane): lane l's bytes land at LDS address lds + 16*l.  M0 carries the LDS
+// address and is restored afterwards.
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Waits until the loads of at most `newer` tiles (K loads each) are still in flight.
+template <int K, int MAXN>
+__device__ __forceinline__ void wait_tiles(int newer) {
+  if constexpr (MAXN == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (newer >= MAXN) wait_vmcnt<K * MAXN>();
+    else wait_tiles<K, MAXN - 1>(newer);
+  }
+}
+
+template <int D, bool FP8, int MT, int NW, int ST>
 struct Cfg {
   static constexpr int kEsz = FP8 ? 1 : 2;
-  static constexpr int kRowBytes = D * kEsz;               // one token row of K or V
-  static constexpr int kChunks = kRowBytes / 16;           // 16-byte chunks per row
-  static constexpr int kTensorBytes = kTile * kRowBytes;   // K or V tile
+  static constexpr int kRowBytes = D * kEsz;              // one token row of K or V
+  static constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per row
+  static constexpr int kTensorBytes = kTK * kRowBytes;    // K or V tile
   static constexpr int kStageBytes = 2 * kTensorBytes;
   static constexpr int kThreads = NW * kWave;
-  static constexpr int kTotalChunks = 2 * kTile * kChunks;  // K and V of one tile
-  static constexpr int kChunksPerThread = (kTotalChunks + kThreads - 1) / kThreads;
-  static constexpr bool kRagged = kTotalChunks % kThreads != 0;
-  static constexpr int kDc = D / 32;                        // MFMA k-steps over d
-  static constexpr int kDt = D / 16;                        // 16-wide d tiles of O
+  static constexpr int kDmaPerTensor = kTensorBytes / (16 * kThreads);  // per lane
+  static constexpr int kDmaPerTile = 2 * kDmaPerTensor;
+  static constexpr int kDc = D / 32;                       // MFMA k-steps over d
+  static constexpr int kDt = D / 16;                       // 16-wide d tiles of O
+  static_assert(kTensorBytes % (16 * kThreads) == 0, "tile must split evenly into DMA slots");
+  static_assert(kDmaPerTile * (ST - 2) < 64, "vmcnt range");
+  static_assert(ST >= 2 && ST <= 4, "2..4 stages");
 };
 
-template <int D, bool FP8, int NW>
-__global__ __launch_bounds__(NW * kWave) void k_attn(Params p) {
-  using C = Cfg<D, FP8, NW>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::kStageBytes];
+template <int D, bool FP8, int MT, int NW, int ST>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2))) void k_attn(Params p) {
+  using C = Cfg<D, FP8, MT, NW, ST>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[ST * C::kStageBytes];
 
-  // XCD-aware work order: workgroup b runs on XCD b % 8; give each XCD a contiguous
+  // XCD-aware work order: workgroup b runs on XCD b % 8; each XCD gets a contiguous
   // range of items (KV-head-major), so one XCD's L2 serves neighbouring groups of the
   // same KV head.
   const int b = blockIdx.x;
@@ -118,11 +164,11 @@ __global__ __launch_bounds__(NW * kWave) void k_attn(Params p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform per wave
   const int li = lane & 15;      // MFMA row/col index inside a 16-lane group
   const int lq = lane >> 4;      // 16-lane group 0..3
 
-  // ---- members and this lane's query row ------------------------------------------
+  // ---- members and this lane's query rows -------------------------------------------
   int gsize;
   const int32_t* qids = nullptr;
   if (p.group_qids) {
@@ -131,35 +177,41 @@ __global__ __launch_bounds__(NW * kWave) void k_attn(Params p) {
   } else {
     gsize = min(p.max_group, p.nq - j * p.max_group);
   }
-  const int row = wave * 16 + li;
-  const int member = row / p.G;
-  const int h = g * p.G + (row - member * p.G);
-  int qid = -1;
-  if (member < gsize) qid = qids ? qids[member] : j * p.max_group + member;
-  if (qid >= p.nq) qid = -1;
-  const bool row_valid = qid >= 0;
-  const int qpos = row_valid ? p.q_pos[qid] : -1;
-  const int row_lim = min(qpos, p.kv_len - 1);   // last usable token of this row
-
-  // members owned by this wave (bit m) and the wave's last usable token
-  int wave_members = 0;
-  for (int r = wave * 16; r < wave * 16 + 16; ++r) {
-    const int m = r / p.G;
-    if (m < gsize) wave_members |= 1 << m;
-  }
-  int wave_lim = row_lim;
+  int qid[MT], hh[MT], row_lim[MT], my_bit[MT], mt_members[MT], mt_lim[MT];
+  bf16x8 qf[MT][C::kDc];
 #pragma unroll
-  for (int o = 1; o < 16; o <<= 1) wave_lim = max(wave_lim, __shfl_xor(wave_lim, o, kWave));
-
-  // ---- Q^T fragments (B operand of S^T = K . Q^T): row li, d = 32c + 8lq .. +8 ------
-  bf16x8 qf[C::kDc];
+  for (int m = 0; m < MT; ++m) {
+    const int row0 = 16 * (wave * MT + m);
+    const int row = row0 + li;
+    const int member = row / p.G;
+    hh[m] = g * p.G + (row - member * p.G);
+    int id = -1;
+    if (member < gsize) id = qids ? qids[member] : j * p.max_group + member;
+    if (id >= p.nq) id = -1;
+    qid[m] = id;
+    const int qpos = id >= 0 ? p.q_pos[id] : -1;
+    row_lim[m] = min(qpos, p.kv_len - 1);          // last usable token of this row
+    my_bit[m] = id >= 0 ? (1 << member) : 0;
+    int mm = 0;
+    for (int r = row0; r < row0 + 16; ++r) {
+      const int mb = r / p.G;
+      if (mb < gsize) mm |= 1 << mb;
+    }
+    mt_members[m] = __builtin_amdgcn_readfirstlane(mm);   // same in every lane
+    int lim = row_lim[m];
 #pragma unroll
-  for (int c = 0; c < C::kDc; ++c) {
-    if (row_valid) {
-      const i32x4 v = *reinterpret_cast<const i32x4*>(p.q + ((int64_t)qid * p.hq + h) * D + 32 * c + 8 * lq);
-      qf[c] = __builtin_bit_cast(bf16x8, v);
-    } else {
-      qf[c] = bf16x8{};
+    for (int o = 1; o < 16; o <<= 1) lim = max(lim, __shfl_xor(lim, o, kWave));
+    mt_lim[m] = __builtin_amdgcn_readfirstlane(lim);      // same in every lane
+    // Q^T fragments (B operand of S^T = K . Q^T): row li, d = 32c + 8lq .. +8
+#pragma unroll
+    for (int c = 0; c < C::kDc; ++c) {
+      if (id >= 0) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(p.q + ((int64_t)id * p.hq + hh[m]) * D +
+                                                         32 * c + 8 * lq);
+        qf[m][c] = __builtin_bit_cast(bf16x8, v);
+      } else {
+        qf[m][c] = bf16x8{};
+      }
     }
   }
 
@@ -167,225 +219,293 @@ __global__ __launch_bounds__(NW * kWave) void k_attn(Params p) {
   const int table = p.shared_table ? g : item;
   const int64_t e_begin = min<int64_t>(max(p.union_off[table], 0), p.capacity);
   const int64_t e_end = min<int64_t>(p.union_off[table + 1], p.capacity);
-  const int tpp = p.page_size / kTile;                       // tiles per page
-  const int n_tiles = (int)max<int64_t>(e_end - e_begin, 0) * tpp;
+  const int tpp_shift = p.page_size == 128 ? 2 : 1;          // log2(tiles per page)
+  const int n_tiles = (int)max<int64_t>(e_end - e_begin, 0) << tpp_shift;
 
   const uint8_t* kbase = p.k_cache + (int64_t)g * p.stride_head_b;
   const uint8_t* vbase = p.v_cache + (int64_t)g * p.stride_head_b;
+  // metadata through the scalar cache (constant address space): uniform per tile
+  const PW_CONST int32_t* cpages = (const PW_CONST int32_t*)p.union_pages;
+  const PW_CONST uint8_t* cqmask = (const PW_CONST uint8_t*)p.union_qmask;
+  const PW_CONST float* cks = (const PW_CONST float*)p.k_scale;
+  const PW_CONST float* cvs = (const PW_CONST float*)p.v_scale;
 
-  // per-tile metadata, uniform over the workgroup
-  struct Meta { int page, sub, qm; float ks, vs; };
-  auto meta_of = [&](int t) -> Meta {
-    Meta m;
-    const int64_t e = e_begin + t / tpp;
-    m.sub = t - (t / tpp) * tpp;
-    m.page = p.union_pages[e];
-    m.qm = p.union_qmask ? p.union_qmask[e] : 0xFF;
-    if (m.page < 0 || m.page >= p.n_pages) { m.page = -1; m.qm = 0; }
-    m.ks = 1.0f;
-    m.vs = 1.0f;
-    if (FP8 && m.page >= 0) {
-      m.ks = p.k_scale[(int64_t)g * p.n_pages + m.page];
-      m.vs = p.v_scale[(int64_t)g * p.n_pages + m.page];
-    }
-    return m;
-  };
+  // per-lane byte offsets of this lane's DMA slots inside one K (or V) tile
+  uint32_t dma_off[C::kDmaPerTensor];
+#pragma unroll
+  for (int i = 0; i < C::kDmaPerTensor; ++i) {
+    const int slot = (i * NW + wave) * kWave + lane;
+    const int r = slot / C::kChunks;
+    const int pc = slot - r * C::kChunks;
+    dma_off[i] = r * C::kRowBytes + ((pc ^ swz<C::kChunks>(r)) << 4);
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(PW_LDS void*)lds;
+  const PW_LDS uint8_t* lds_p = (const PW_LDS uint8_t*)lds;
 
-  // ---- staging: global -> registers -> LDS ------------------------------------------
-  i32x4 stage_regs[C::kChunksPerThread];
-  auto load_tile = [&](const Meta& m) {
-    if (m.page < 0) return;
-    const int64_t off = (int64_t)m.page * p.stride_page_b + (int64_t)m.sub * kTile * C::kRowBytes;
+  // per-lane LDS read offsets inside one stage (the stage base is an immediate)
+  int k_off[2][C::kDc];
 #pragma unroll
-    for (int i = 0; i < C::kChunksPerThread; ++i) {
-      const int cid = tid + i * C::kThreads;                 // 0 .. kTotalChunks-1
-      if (C::kRagged && cid >= C::kTotalChunks) break;
-      const int tensor = cid / (kTile * C::kChunks);
-      const int rem = cid - tensor * (kTile * C::kChunks);
-      const uint8_t* src = (tensor ? vbase : kbase) + off + (int64_t)rem * 16;
-      stage_regs[i] = *reinterpret_cast<const i32x4*>(src);
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = 8 * (li >> 2) + 4 * kb + (li & 3);   // MFMA row li of key block kb
+#pragma unroll
+    for (int c = 0; c < C::kDc; ++c) {
+      const int byte = (32 * c + 8 * lq) * C::kEsz;
+      k_off[kb][c] = key * C::kRowBytes + (((byte >> 4) ^ swz<C::kChunks>(key)) << 4) + (byte & 15);
     }
+  }
+  constexpr int kVr = FP8 ? C::kDt : 2 * C::kDt;
+  int v_off[kVr];
+#pragma unroll
+  for (int dt = 0; dt < C::kDt; ++dt) {
+    if constexpr (FP8) {
+      // ds_read_b64_tr_b8: output byte e of lane li = V[8*lq + e][16*dt + li] when source
+      // lane li reads key 8*lq + (li >> 1), columns 16*dt + 8*(li & 1) .. +8
+      const int key = 8 * lq + (li >> 1);
+      const int byte = 16 * dt + 8 * (li & 1);
+      v_off[dt] = C::kTensorBytes + key * C::kRowBytes + (((byte >> 4) ^ swz<C::kChunks>(key)) << 4) + (byte & 15);
+    } else {
+      // ds_read_b64_tr_b16: output element e of lane li = V[key0 + e][16*dt + li] when
+      // source lane li reads key key0 + (li >> 2), columns 16*dt + 4*(li & 3) .. +4
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int key = 8 * lq + 4 * hf + (li >> 2);
+        const int byte = (16 * dt + 4 * (li & 3)) * 2;
+        v_off[2 * dt + hf] = C::kTensorBytes + key * C::kRowBytes + (((byte >> 4) ^ swz<C::kChunks>(key)) << 4) + (byte & 15);
+      }
+    }
+  }
+
+  auto page_of = [&](int t) -> int {
+    const int pg = cpages[e_begin + (t >> tpp_shift)];
+    return (pg >= 0 && pg < p.n_pages) ? pg : -1;
   };
-  auto store_tile = [&](int stage, const Meta& m) {
-    if (m.page < 0) return;
-    uint8_t* dst = lds + stage * C::kStageBytes;
+  // Every tile issues the same number of loads (an invalid page reads page 0 and is
+  // never computed), so the vmcnt waits below are exact.
+  auto issue = [&](int t, auto stage_c) {
+    constexpr int SS = decltype(stage_c)::value;
+    const int pg = max(page_of(t), 0);
+    const int64_t off = (int64_t)pg * p.stride_page_b + (int64_t)(t & ((1 << tpp_shift) - 1)) * C::kTensorBytes;
+    const uint8_t* kt = kbase + off;
+    const uint8_t* vt = vbase + off;
 #pragma unroll
-    for (int i = 0; i < C::kChunksPerThread; ++i) {
-      const int cid = tid + i * C::kThreads;
-      if (C::kRagged && cid >= C::kTotalChunks) break;
-      const int tensor = cid / (kTile * C::kChunks);
-      const int rem = cid - tensor * (kTile * C::kChunks);
-      const int r = rem / C::kChunks;
-      const int ch = rem - r * C::kChunks;
-      *reinterpret_cast<i32x4*>(dst + tensor * C::kTensorBytes + r * C::kRowBytes +
-                                ((ch ^ swz<C::kChunks>(r)) << 4)) = stage_regs[i];
-    }
+    for (int i = 0; i < C::kDmaPerTensor; ++i)
+      dma16(dma_off[i], kt, lds_base + SS * C::kStageBytes + (i * NW + wave) * (kWave * 16));
+#pragma unroll
+    for (int i = 0; i < C::kDmaPerTensor; ++i)
+      dma16(dma_off[i], vt, lds_base + SS * C::kStageBytes + C::kTensorBytes + (i * NW + wave) * (kWave * 16));
   };
 
   // ---- running state ------------------------------------------------------------------
-  f32x4 o[C::kDt];
+  f32x4 o[MT][C::kDt];
+  float m_ref[MT], l_run[MT];
+  int mt_min[MT];   // smallest usable last token over the valid rows of a row tile
 #pragma unroll
-  for (int t = 0; t < C::kDt; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-  const int my_bit = row_valid ? (1 << member) : 0;
-
-  Meta cur = n_tiles > 0 ? meta_of(0) : Meta{-1, 0, 0, 1.f, 1.f};
-  if (n_tiles > 0) {
-    load_tile(cur);
-    store_tile(0, cur);
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int dt = 0; dt < C::kDt; ++dt) o[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_ref[m] = -INFINITY;
+    l_run[m] = 0.f;
+    int lim = qid[m] >= 0 ? row_lim[m] : 0x7fffffff;
+#pragma unroll
+    for (int sh = 1; sh < 16; sh <<= 1) lim = min(lim, __shfl_xor(lim, sh, kWave));
+    mt_min[m] = __builtin_amdgcn_readfirstlane(lim);
   }
-  __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int stage = t & 1;
-    Meta nxt{-1, 0, 0, 1.f, 1.f};
-    if (t + 1 < n_tiles) {
-      nxt = meta_of(t + 1);
-      load_tile(nxt);
+  // Make every earlier global load complete here, before the first direct-to-LDS load is
+  // issued: the compiler does not see those loads, so a wait it placed later for its own
+  // loads would also wait for the whole ring.
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int c = 0; c < C::kDc; ++c) asm volatile("" ::"v"(__builtin_bit_cast(i32x4, qf[m][c])));
+    asm volatile("" ::"v"(row_lim[m]), "v"(qid[m]));
+  }
+
+  // ---- one tile: S^T = K Q^T, masked online softmax, O^T += V^T P^T --------------------
+  auto compute = [&](int t, auto stage_c) {
+    constexpr int SS = decltype(stage_c)::value;
+    const int pg = page_of(t);
+    const int tok0 = pg * p.page_size + (t & ((1 << tpp_shift) - 1)) * kTK;
+    int qm = 0xFF;
+    if (cqmask) {   // member-mask byte, read through an aligned scalar dword load
+      const int64_t e = e_begin + (t >> tpp_shift);
+      const uint32_t w4 = ((const PW_CONST uint32_t*)cqmask)[e >> 2];
+      qm = (int)((w4 >> (8 * (int)(e & 3))) & 0xFF);
     }
-    const int tok0 = cur.page * p.page_size + cur.sub * kTile;
-    const bool wave_active = cur.page >= 0 && (cur.qm & wave_members) != 0 && tok0 <= wave_lim;
-    if (wave_active) {
-      const uint8_t* kt = lds + stage * C::kStageBytes;
-      const uint8_t* vt = kt + C::kTensorBytes;
-      // S^T blocks: MFMA row i of key block kb holds key pi(kb, i)
-      f32x4 s[4];
+    bool act[MT];
+    bool any = false;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int key = 32 * (kb >> 1) + 8 * (li >> 2) + 4 * (kb & 1) + (li & 3);
-        const uint8_t* krow = kt + key * C::kRowBytes;
+    for (int m = 0; m < MT; ++m) {
+      act[m] = pg >= 0 && (qm & mt_members[m]) != 0 && tok0 <= mt_lim[m];
+      any |= act[m];
+    }
+    if (!any) return;
+    float ks = 1.f, vs = 1.f;
+    if constexpr (FP8) {
+      ks = cks[(int64_t)g * p.n_pages + pg];
+      vs = cvs[(int64_t)g * p.n_pages + pg];
+    }
+    const float sc = p.score_scale * ks;                      // log2-domain score scale
+    const float lvs = FP8 ? __builtin_amdgcn_logf(vs) : 0.f;  // log2 of the V page scale
+    const float inv_vs = FP8 ? 1.0f / vs : 1.f;
+    const PW_LDS uint8_t* st = lds_p + SS * C::kStageBytes;
+
+    // K fragments (A operand of S^T = K . Q^T), shared by every row tile
+    bf16x8 ka[2][C::kDc];
 #pragma unroll
-        for (int c = 0; c < C::kDc; ++c) {
-          const int byte = (32 * c + 8 * lq) * C::kEsz;
-          const int ch = byte >> 4;
-          const uint8_t* src = krow + ((ch ^ swz<C::kChunks>(key)) << 4) + (byte & 15);
-          bf16x8 a;
-          if constexpr (FP8) {
-            a = fp8x8_to_bf16(*reinterpret_cast<const i32x2*>(src));
-          } else {
-            a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(src));
-          }
-          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], s[kb], 0, 0, 0);
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < C::kDc; ++c) {
+        if constexpr (FP8) {
+          ka[kb][c] = fp8x8_to_bf16(*reinterpret_cast<const PW_LDS i32x2*>(st + k_off[kb][c]));
+        } else {
+          ka[kb][c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const PW_LDS i32x4*>(st + k_off[kb][c]));
         }
       }
-      // lane holds row li and keys 32*(kb>>1) + 8*lq + 4*(kb&1) + ii
-      const bool sel = (cur.qm & my_bit) != 0;
-      const float sc = p.score_scale * cur.ks;
-      const bool full = tok0 + kTile - 1 <= row_lim;
-      float mloc = -INFINITY;
+
+    bf16x8 pf[MT];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+    for (int m = 0; m < MT; ++m) {
+      pf[m] = bf16x8{};
+      if (!act[m]) continue;
+      f32x4 s2[2];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int key = 32 * (kb >> 1) + 8 * lq + 4 * (kb & 1) + ii;
-          const bool ok = sel && (full || tok0 + key <= row_lim);
-          const float v = ok ? s[kb][ii] * sc : -INFINITY;
-          s[kb][ii] = v;
-          mloc = fmaxf(mloc, v);
-        }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-      const float m_new = fmaxf(m_run, mloc);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      for (int kb = 0; kb < 2; ++kb) {
+        s2[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < C::kDc; ++c)
+          s2[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][c], qf[m][c], s2[kb], 0, 0, 0);
+      }
+      // lane holds row li of tile m and tile keys 8*lq + 4*kb + ii
+      const bool sel = (qm & my_bit[m]) != 0;
+      const bool row_any = sel && tok0 <= row_lim[m];
+      const bool tile_full = tok0 + kTK - 1 <= mt_min[m];          // uniform
+      auto scores = [&](float bias, float* x) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            float v = __builtin_fmaf(s2[kb][ii], sc, bias);
+            if (!tile_full && tok0 + 8 * lq + 4 * kb + ii > row_lim[m]) v = -INFINITY;
+            x[4 * kb + ii] = v;
+          }
+      };
+      // fast path: P = exp2(s*sc - m_ref + log2 vs) with the current reference
+      float pv[8];
+      scores(sel && m_ref[m] != -INFINITY ? lvs - m_ref[m] : -INFINITY, pv);
+      float pmax = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        pv[k] = __builtin_amdgcn_exp2f(pv[k]);
+        pmax = fmaxf(pmax, pv[k]);
+      }
+      pmax = fmaxf(pmax, __shfl_xor(pmax, 16, kWave));
+      pmax = fmaxf(pmax, __shfl_xor(pmax, 32, kWave));
+      // the reference must be set (first used tile of a row) or raised (a score exceeds it
+      // by more than 2^8): rare, wave-uniform slow path
+      const bool need = row_any && (m_ref[m] == -INFINITY || !(pmax <= 256.f * vs));
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        float raw[8];
+        scores(sel ? 0.f : -INFINITY, raw);
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) mloc = fmaxf(mloc, raw[k]);
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+        const bool raise = row_any && (m_ref[m] == -INFINITY || mloc > m_ref[m] + kRescaleMargin);
+        const float m_new = raise ? mloc : m_ref[m];
+        const float alpha = m_ref[m] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref[m] - m_new);
+        l_run[m] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < C::kDt; ++dt) o[m][dt] *= alpha;
+        m_ref[m] = m_new;
+        const float bias = (sel && m_new != -INFINITY) ? lvs - m_new : -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) pv[k] = __builtin_amdgcn_exp2f(raw[k] + bias);
+      }
       float lsum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const float e = __builtin_amdgcn_exp2f(s[kb][ii] - m_use);
-          s[kb][ii] = e;
-          lsum += e;
-        }
+      for (int k = 0; k < 8; ++k) {
+        lsum += pv[k];
+        pf[m][k] = (__bf16)pv[k];
+      }
       lsum += __shfl_xor(lsum, 16, kWave);
       lsum += __shfl_xor(lsum, 32, kWave);
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < C::kDt; ++dt) o[dt] *= alpha;
-      // P^T operand (B): chunk c2 covers keys 32*c2 + 8*lq + 0..7 = blocks 2c2 (0..3), 2c2+1 (4..7)
-      bf16x8 pf[2];
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          pf[c2][ii] = (__bf16)(s[2 * c2][ii] * cur.vs);
-          pf[c2][4 + ii] = (__bf16)(s[2 * c2 + 1][ii] * cur.vs);
-        }
-      }
-      // O^T[d][row] += V^T . P^T ; A operand lane li = d column, keys 32*c2 + 8*lq + 0..7
-#pragma unroll
-      for (int dt = 0; dt < C::kDt; ++dt) {
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          bf16x8 a;
-          if constexpr (FP8) {
-            // byte e of output lane li = V[key0 + e][16*dt + li]; source lane li reads
-            // key0 + (li >> 1), columns 16*dt + 8*(li & 1) .. +8
-            const int key = 32 * c2 + 8 * lq + (li >> 1);
-            const int byte = 16 * dt + 8 * (li & 1);
-            const uint8_t* src = vt + key * C::kRowBytes + (((byte >> 4) ^ swz<C::kChunks>(key)) << 4) + (byte & 15);
-            const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PW_LDS i32x2*)(src));
-            a = fp8x8_to_bf16(raw);
-          } else {
-            // element e of output lane li = V[key0 + e][16*dt + li]; source lane li reads
-            // key0 + (li >> 2), columns 16*dt + 4*(li & 3) .. +4
-            bf16x4 lo, hi;
-            {
-              const int key = 32 * c2 + 8 * lq + (li >> 2);
-              const int byte = (16 * dt + 4 * (li & 3)) * 2;
-              const uint8_t* src = vt + key * C::kRowBytes + (((byte >> 4) ^ swz<C::kChunks>(key)) << 4) + (byte & 15);
-              lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PW_LDS bf16x4*)(src));
-            }
-            {
-              const int key = 32 * c2 + 8 * lq + 4 + (li >> 2);
-              const int byte = (16 * dt + 4 * (li & 3)) * 2;
-              const uint8_t* src = vt + key * C::kRowBytes + (((byte >> 4) ^ swz<C::kChunks>(key)) << 4) + (byte & 15);
-              hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PW_LDS bf16x4*)(src));
-            }
-            a = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[c2], o[dt], 0, 0, 0);
-        }
-      }
+      l_run[m] += lsum * inv_vs;
     }
-    if (t + 1 < n_tiles) store_tile(stage ^ 1, nxt);
-    __syncthreads();
-    cur = nxt;
-  }
 
-  // ---- epilogue: rows to their original IDs ------------------------------------------
-  if (row_valid) {
-    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-    uint16_t* dst = p.out + ((int64_t)qid * p.hq + h) * D;
+    // O^T[d][row] += V^T . P^T for every row tile (an unused tile has P = 0): A operand
+    // lane li = d column 16*dt + li, k-slots e = tile keys 8*lq + e
 #pragma unroll
     for (int dt = 0; dt < C::kDt; ++dt) {
-      const bf16x4 v{(__bf16)(o[dt][0] * inv), (__bf16)(o[dt][1] * inv), (__bf16)(o[dt][2] * inv),
-                     (__bf16)(o[dt][3] * inv)};
+      bf16x8 a;
+      if constexpr (FP8) {
+        a = fp8x8_to_bf16(__builtin_amdgcn_ds_read_tr8_b64_v2i32((PW_LDS i32x2*)(st + v_off[dt])));
+      } else {
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PW_LDS bf16x4*)(st + v_off[2 * dt]));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PW_LDS bf16x4*)(st + v_off[2 * dt + 1]));
+        a = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        o[m][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[m], o[m][dt], 0, 0, 0);
+    }
+  };
+
+  // ---- pipeline: tile t lives in stage t % ST; the loop is unrolled by ST so that every
+  // stage offset is a compile-time immediate ------------------------------------------------
+  auto step = [&](int t, auto stage_c) {
+    constexpr int SS = decltype(stage_c)::value;
+    wait_tiles<C::kDmaPerTile, ST - 2>(min(n_tiles - 1 - t, ST - 2));   // tile t has landed
+    if constexpr (NW > 1) __builtin_amdgcn_s_barrier();                 // ... for every wave
+    if (t + ST - 1 < n_tiles) issue(t + ST - 1, std::integral_constant<int, (SS + ST - 1) % ST>{});
+    compute(t, stage_c);
+  };
+  if (0 < n_tiles) issue(0, std::integral_constant<int, 0>{});
+  if constexpr (ST > 2) if (1 < n_tiles) issue(1, std::integral_constant<int, 1>{});
+  if constexpr (ST > 3) if (2 < n_tiles) issue(2, std::integral_constant<int, 2>{});
+  for (int t0 = 0; t0 < n_tiles; t0 += ST) {
+    step(t0, std::integral_constant<int, 0>{});
+    if (t0 + 1 < n_tiles) step(t0 + 1, std::integral_constant<int, 1>{});
+    if constexpr (ST > 2) if (t0 + 2 < n_tiles) step(t0 + 2, std::integral_constant<int, 2>{});
+    if constexpr (ST > 3) if (t0 + 3 < n_tiles) step(t0 + 3, std::integral_constant<int, 3>{});
+  }
+  wait_vmcnt<0>();
+
+  // ---- epilogue: rows to their original IDs ------------------------------------------
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (qid[m] < 0) continue;
+    const float inv = l_run[m] > 0.f ? 1.0f / l_run[m] : 0.f;
+    uint16_t* dst = p.out + ((int64_t)qid[m] * p.hq + hh[m]) * D;
+#pragma unroll
+    for (int dt = 0; dt < C::kDt; ++dt) {
+      const bf16x4 v{(__bf16)(o[m][dt][0] * inv), (__bf16)(o[m][dt][1] * inv),
+                     (__bf16)(o[m][dt][2] * inv), (__bf16)(o[m][dt][3] * inv)};
       *reinterpret_cast<bf16x4*>(dst + 16 * dt + 4 * lq) = v;
     }
     if (p.lse && lq == 0)
-      p.lse[(int64_t)qid * p.hq + h] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+      p.lse[(int64_t)qid[m] * p.hq + hh[m]] =
+          l_run[m] > 0.f ? (m_ref[m] + __log2f(l_run[m])) * kLn2 : -INFINITY;
   }
 }
 
-template <int D, bool FP8, int NW>
+template <int D, bool FP8, int MT, int NW, int ST>
 pw_status launch_t(const Params& p, hipStream_t stream) {
   const int grid = 8 * p.items_per_xcd;
-  hipLaunchKernelGGL((k_attn<D, FP8, NW>), dim3(grid), dim3(NW * kWave), 0, stream, p);
+  hipLaunchKernelGGL((k_attn<D, FP8, MT, NW, ST>), dim3(grid), dim3(NW * kWave), 0, stream, p);
   return check_launch("sparse_prefill");
 }
 
+// Row tiling: <= 16 rows -> one wave, one row tile; <= 32 -> one wave, two row tiles;
+// <= 64 -> two waves of two row tiles.
 template <int D, bool FP8>
-pw_status launch_d(const Params& p, int nw, hipStream_t stream) {
-  switch (nw) {
-    case 1: return launch_t<D, FP8, 1>(p, stream);
-    case 2: return launch_t<D, FP8, 2>(p, stream);
-    case 3: return launch_t<D, FP8, 3>(p, stream);
-    case 4: return launch_t<D, FP8, 4>(p, stream);
-  }
-  return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: %d waves", nw);
+pw_status launch_d(const Params& p, int rows, hipStream_t stream) {
+  constexpr int ST = FP8 ? 3 : 2;
+  if (rows <= 16) return launch_t<D, FP8, 1, 1, ST>(p, stream);
+  if (rows <= 32) return launch_t<D, FP8, 2, 1, ST>(p, stream);
+  if (rows <= 64) return launch_t<D, FP8, 2, 2, ST>(p, stream);
+  return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: %d rows per group", rows);
 }
 
 }  // namespace
@@ -424,10 +544,9 @@ pw_status launch_sparse_prefill(const AttnArgs& a, hipStream_t stream) {
   p.score_scale = a.sm_scale * kLog2e;
   if (p.n_items == 0) return PW_OK;
   const int rows = a.max_group * p.G;
-  const int nw = (rows + 15) / 16;
   const bool fp8 = a.kv_dtype == PW_KV_FP8_E4M3;
-  if (a.d == 128) return fp8 ? launch_d<128, true>(p, nw, stream) : launch_d<128, false>(p, nw, stream);
-  if (a.d == 64) return fp8 ? launch_d<64, true>(p, nw, stream) : launch_d<64, false>(p, nw, stream);
+  if (a.d == 128) return fp8 ? launch_d<128, true>(p, rows, stream) : launch_d<128, false>(p, rows, stream);
+  if (a.d == 64) return fp8 ? launch_d<64, true>(p, rows, stream) : launch_d<64, false>(p, rows, stream);
   return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: d=%d", a.d);
 }
 

@@ -66,7 +66,8 @@ __global__ void k_page_bitsets(const int32_t* __restrict__ topk, int n_rows, int
   const int wave = threadIdx.x / kWave;
   const int waves = blockDim.x / kWave;
   uint8_t* flags = flags_all + (size_t)wave * words * kWave;
-  for (int i = lane; i < words * kWave; i += kWave) flags[i] = 0;
+  for (int i = lane * 16; i < words * kWave; i += kWave * 16)
+    *reinterpret_cast<uint4*>(flags + i) = make_uint4(0, 0, 0, 0);
   wave_lds_sync();
 
   const int64_t total = (int64_t)n_rows * hkv;
@@ -172,6 +173,85 @@ __global__ void k_group(const uint64_t* __restrict__ bits, int nq, int words, in
       for (int j = 1; j < 8; ++j) if (j == cnt) members[j] = pick;
       ++cnt;
       --remaining;
+    }
+    if (c < max_group) {
+      int v = -1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) if (j == c && j < cnt) v = start + members[j];
+      group_qids[(gbase + gi) * max_group + c] = v;
+    }
+    if (c == 0) group_size[gbase + gi] = cnt;
+    ++gi;
+  }
+}
+
+// Wave-wide maximum by DPP: row_shr 1/2/4/8 gives every 16-lane row its maximum in
+// lane 15, row_bcast 15/31 folds the rows into lane 63, which is read back.
+__device__ __forceinline__ int wave_max_dpp(int v) {
+  constexpr int kLow = -2147483647 - 1;
+  v = max(v, __builtin_amdgcn_update_dpp(kLow, v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = max(v, __builtin_amdgcn_update_dpp(kLow, v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = max(v, __builtin_amdgcn_update_dpp(kLow, v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = max(v, __builtin_amdgcn_update_dpp(kLow, v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  v = max(v, __builtin_amdgcn_update_dpp(kLow, v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, __builtin_amdgcn_update_dpp(kLow, v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Same search for windows of at most 64 candidates: one wave per (window, KV head), the
+// group union U held in scalar registers (wave-uniform), candidates' bitsets in their
+// lanes, the free set as a 64-bit lane mask, and the argmax key (overlap << 6 | 63 - c)
+// reduced with DPP.  No LDS and no barriers on the pick chain.
+template <int MAXW>
+__global__ __launch_bounds__(64) void k_group_wave(const uint64_t* __restrict__ bits, int nq,
+                                                   int words, int window, int max_group,
+                                                   int n_groups, int32_t* __restrict__ group_qids,
+                                                   int32_t* __restrict__ group_size) {
+  const int g = blockIdx.y;
+  const int start = blockIdx.x * window;
+  const int len = min(window, nq - start);
+  const int c = threadIdx.x;
+  const bool valid = c < len;
+  uint32_t lo[MAXW], hi[MAXW];
+  const uint64_t* row = bits + ((int64_t)g * nq + start + c) * words;
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w) {
+    const uint64_t x = (valid && w < words) ? row[w] : 0ull;
+    lo[w] = (uint32_t)x;
+    hi[w] = (uint32_t)(x >> 32);
+  }
+  uint64_t free_mask = __ballot(valid);
+  const int64_t gbase = (int64_t)g * n_groups + (int64_t)blockIdx.x * (window / max_group);
+  int gi = 0;
+  while (free_mask) {
+    const int seed = __builtin_ctzll(free_mask);           // lowest ungrouped ID
+    free_mask &= free_mask - 1;
+    uint32_t ulo[MAXW], uhi[MAXW];
+#pragma unroll
+    for (int w = 0; w < MAXW; ++w) {
+      ulo[w] = __builtin_amdgcn_readlane(lo[w], seed);
+      uhi[w] = __builtin_amdgcn_readlane(hi[w], seed);
+    }
+    int members[8];
+    members[0] = seed;
+    int cnt = 1;
+    while (cnt < max_group && free_mask) {
+      int score = 0;
+#pragma unroll
+      for (int w = 0; w < MAXW; ++w)
+        if (w < words) score += __builtin_popcount(lo[w] & ulo[w]) + __builtin_popcount(hi[w] & uhi[w]);
+      const bool is_free = (free_mask >> c) & 1ull;
+      const int best = wave_max_dpp(is_free ? ((score << 6) | (63 - c)) : -1);
+      const int pick = 63 - (best & 63);
+      free_mask &= ~(1ull << pick);
+#pragma unroll
+      for (int w = 0; w < MAXW; ++w) {
+        ulo[w] |= __builtin_amdgcn_readlane(lo[w], pick);
+        uhi[w] |= __builtin_amdgcn_readlane(hi[w], pick);
+      }
+#pragma unroll
+      for (int j = 1; j < 8; ++j) if (j == cnt) members[j] = pick;
+      ++cnt;
     }
     if (c < max_group) {
       int v = -1;
@@ -303,7 +383,7 @@ pw_status launch_page_bitsets(const int32_t* topk, int n_rows, int hkv, int k, i
   const int per_wave = words * kWave;
   const int waves = std::max(1, std::min(4, 65536 / per_wave));
   const int64_t want = (total + waves - 1) / waves;
-  const int blocks = (int)std::min<int64_t>(want, 8192);
+  const int blocks = (int)std::min<int64_t>(want, 1024);
   hipLaunchKernelGGL(k_page_bitsets, dim3(blocks), dim3(waves * kWave),
                      (size_t)waves * per_wave, stream, topk, n_rows, hkv, k, n_pages, words, bits,
                      bad_id_count);
@@ -316,6 +396,21 @@ pw_status launch_group(const uint64_t* bits, int nq, int hkv, int n_pages, int w
   if (nq == 0) return PW_OK;
   const int words = (n_pages + 63) / 64;
   const int n_windows = (nq + window - 1) / window;
+  if (window <= 64) {
+    dim3 grid(n_windows, hkv), block(64);
+#define PW_GROUPW_CASE(W)                                                                    \
+    if (words <= W) {                                                                        \
+      hipLaunchKernelGGL(k_group_wave<W>, grid, block, 0, stream, bits, nq, words, window,  \
+                         max_group, n_groups, group_qids, group_size);                       \
+      return check_launch("group");                                                          \
+    }
+    PW_GROUPW_CASE(1)
+    PW_GROUPW_CASE(2)
+    PW_GROUPW_CASE(4)
+    PW_GROUPW_CASE(8)
+    PW_GROUPW_CASE(16)   // beyond 16 words the union no longer fits in scalar registers
+#undef PW_GROUPW_CASE
+  }
   const int threads = ((std::min(window, nq) + kWave - 1) / kWave) * kWave;
   dim3 grid(n_windows, hkv), block(threads);
 #define PW_GROUP_CASE(W)                                                                     \
