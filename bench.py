@@ -156,9 +156,10 @@ def main():
     ids_np = w.topk if w.topk is not None else w.mask_rows
     ids = torch.from_numpy(np.ascontiguousarray(ids_np)).to(dev)
     mode = "topk" if w.topk is not None else "block_union"
+    max_group = cfg.max_group if mode == "topk" else max(1, cfg.item_rows // cfg.g)
     plan = pw.SparsePrefill(nq=cfg.nq, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, n_pages=cfg.n_pages,
                             page_size=cfg.ps, kv_len=cfg.kv_len, k=ids.shape[2], window=cfg.window,
-                            max_group=cfg.max_group, mode=mode,
+                            max_group=max_group, mode=mode,
                             n_rows=ids.shape[0] if mode == "block_union" else 0, device=dev)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
@@ -200,11 +201,15 @@ def main():
     # ---- structure of this call's tables --------------------------------------------------
     off = plan.union_off.cpu().numpy()
     total_pages = int(off[-1])
-    Bu = unique_kv_bytes(total_pages, cfg)
+    # page visits: every work item streams its table once (a shared per-KV-group table
+    # is streamed by each of the KV head's groups)
+    visits = total_pages if mode == "topk" else int(np.diff(off).sum()) * plan.n_groups
+    Bu = unique_kv_bytes(visits, cfg)
     attn_ms = statistics.mean(t_attn)
     achieved = Bu / (attn_ms / 1e3) / 1e9
     extras = {"t_prep_ms_mean": statistics.mean(t_prep), "t_attn_ms_mean": attn_ms,
               "t_attn_ms_median": statistics.median(t_attn), "union_pages": total_pages,
+              "page_visits": visits,
               "unique_kv_bytes": Bu}
     if mode == "topk":
         sizes = np.diff(off)
@@ -250,7 +255,7 @@ def main():
                              "online_cost": t_online - t_fixed, "net_saving": t_orig - t_online}
         exec_rows_pages = float((sizes * gsz).sum()) * cfg.g     # (row, union page) pairs
     else:
-        exec_rows_pages = float(total_pages) * cfg.nq * cfg.g    # every row of a KV head x its table
+        exec_rows_pages = float(visits) * max_group * cfg.g      # item rows x its table pages
     # executed MFMA work: QK and PV, 2 flops per MAC, over every (row, union token)
     exec_flops = 4.0 * cfg.d * cfg.ps * exec_rows_pages
     extras["executed_tflops"] = exec_flops / (attn_ms / 1e3) / 1e12
@@ -279,7 +284,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "hq": cfg.hq, "hkv": cfg.hkv, "d": cfg.d, "page_size": cfg.ps,
                    "kv_len": cfg.kv_len, "nq": cfg.nq, "topk": cfg.k, "kv_dtype": cfg.kv_dtype,
-                   "window": cfg.window, "max_group": cfg.max_group, "seed": w.seed},
+                   "window": cfg.window, "max_group": max_group, "seed": w.seed},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(cfg.name), "kernel": "k_attn",
                      "bytes_per_launch": Bu},

@@ -156,8 +156,11 @@ pw_status pw_union_tables(const uint64_t* bits, int n_rows, int hkv, int n_pages
  * out         bf16 [nq][hq][d]; each row written exactly once if it belongs to
  *             a group; rows of queries in no group are left untouched
  * lse         fp32 [nq][hq] or NULL
- * Limits: d in {64, 128}; page_size in {64, 128}; hq % hkv == 0;
- *         G * max_group <= 64; 1 <= max_group <= 8; n_pages >= 1.                   */
+ * Limits: d in {64, 128}; page_size in {64, 128}; hq % hkv == 0; n_pages >= 1;
+ *   with group_qids or union_qmask: 1 <= max_group <= 8 and G * max_group <= 64;
+ *   with neither (consecutive groups, every member uses every page of its table -
+ *   the dense form over a shared per-KV-group table): max_group <= 256 and
+ *   G * max_group <= 256 rows (bf16, d=128), 128 (fp8 d=128, bf16 d=64), 64 (fp8 d=64).  */
 pw_status pw_sparse_prefill(const void* q, int nq, int hq, int hkv, int d,
                             const void* k_cache, const void* v_cache, int kv_dtype,
                             const float* k_scale, const float* v_scale, int page_size,

@@ -199,7 +199,9 @@ class SparsePrefill:
     member masks -> union attention.
     Block-union mode (``mask_rows`` given, CompactAttention's per-KV-group
     block table): bitsets of the mask rows -> one union over every row of a
-    KV head -> attention of consecutive query groups over that shared table.
+    KV head -> attention of consecutive query groups over that shared table;
+    there ``max_group`` may exceed 8 (up to 256 query-head rows per work item)
+    so that each staged tile serves many rows.
     """
     nq: int
     hq: int

@@ -141,13 +141,19 @@ pw_status pw_sparse_prefill(const void* q, int nq, int hq, int hkv, int d, const
   if (d != 64 && d != 128) return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: d=%d (64 or 128)", d);
   if (page_size != 64 && page_size != 128)
     return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: page_size=%d (64 or 128)", page_size);
-  if (max_group < 1 || max_group > 8)
-    return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: max_group=%d not in 1..8", max_group);
-  const int G = hq / hkv;
-  if (G * max_group > 64)
-    return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: (hq/hkv)*max_group=%d > 64", G * max_group);
   if (kv_dtype != PW_KV_BF16 && kv_dtype != PW_KV_FP8_E4M3)
     return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: kv_dtype=%d", kv_dtype);
+  // Member masks and explicit groups hold up to 8 members; consecutive groups over tables
+  // without member masks (every member uses every page) may be wider.
+  const bool wide_ok = group_qids == nullptr && union_qmask == nullptr;
+  if (max_group < 1 || max_group > (wide_ok ? 256 : 8))
+    return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: max_group=%d not in 1..%d", max_group,
+                wide_ok ? 256 : 8);
+  const int G = hq / hkv;
+  const int max_rows = wide_ok ? pw::max_rows_per_item(d, kv_dtype) : 64;
+  if ((int64_t)G * max_group > max_rows)
+    return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: (hq/hkv)*max_group=%d > %d", G * max_group,
+                max_rows);
   if (shared_table != 0 && shared_table != 1)
     return fail(PW_ERR_ARG, "pw_sparse_prefill: shared_table=%d (0 or 1)", shared_table);
   const int esz = kv_dtype == PW_KV_FP8_E4M3 ? 1 : 2;

@@ -32,6 +32,8 @@
 // into the score scale and the V page scale into P (the row sum uses unscaled P).
 #include <hip/hip_runtime.h>
 
+#include <stdlib.h>
+
 #include <algorithm>
 #include <type_traits>
 
@@ -44,7 +46,10 @@ constexpr int kWave = 64;
 constexpr int kTK = 32;               // tokens per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleMargin = 8.0f;  // log2 units
+// The reference used for the exponentials is raised only when a tile's row sum of P
+// exceeds 2^kRescaleLog2 (P = 2^(score - reference)): well inside fp32/bf16 range, and
+// bf16/fp32 precision is relative, so nothing is lost while P stays below it.
+constexpr float kRescaleLog2 = 32.0f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -140,6 +145,7 @@ struct Cfg {
   static constexpr int kStageBytes = 2 * kTensorBytes;
   static constexpr int kThreads = NW * kWave;
   static constexpr int kDmaPerTensor = kTensorBytes / (16 * kThreads);  // per lane
+  static_assert(kDmaPerTensor >= 1, "every wave issues at least one load per tensor");
   static constexpr int kDmaPerTile = 2 * kDmaPerTensor;
   static constexpr int kDc = D / 32;                       // MFMA k-steps over d
   static constexpr int kDt = D / 16;                       // 16-wide d tiles of O
@@ -191,11 +197,16 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     qid[m] = id;
     const int qpos = id >= 0 ? p.q_pos[id] : -1;
     row_lim[m] = min(qpos, p.kv_len - 1);          // last usable token of this row
-    my_bit[m] = id >= 0 ? (1 << member) : 0;
     int mm = 0;
-    for (int r = row0; r < row0 + 16; ++r) {
-      const int mb = r / p.G;
-      if (mb < gsize) mm |= 1 << mb;
+    if (p.union_qmask) {            // member-mask bit per member (max_group <= 8)
+      my_bit[m] = id >= 0 ? (1 << member) : 0;
+      for (int r = row0; r < row0 + 16; ++r) {
+        const int mb = r / p.G;
+        if (mb < gsize) mm |= 1 << mb;
+      }
+    } else {                        // every member uses every page: one shared bit
+      my_bit[m] = id >= 0 ? 1 : 0;
+      mm = row0 / p.G < gsize ? 1 : 0;
     }
     mt_members[m] = __builtin_amdgcn_readfirstlane(mm);   // same in every lane
     int lim = row_lim[m];
@@ -390,20 +401,20 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
             x[4 * kb + ii] = v;
           }
       };
-      // fast path: P = exp2(s*sc - m_ref + log2 vs) with the current reference
+      // fast path: P = exp2(s*sc - reference + log2 vs) with the current reference
       float pv[8];
       scores(sel && m_ref[m] != -INFINITY ? lvs - m_ref[m] : -INFINITY, pv);
-      float pmax = 0.f;
+      float lsum = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         pv[k] = __builtin_amdgcn_exp2f(pv[k]);
-        pmax = fmaxf(pmax, pv[k]);
+        lsum += pv[k];
       }
-      pmax = fmaxf(pmax, __shfl_xor(pmax, 16, kWave));
-      pmax = fmaxf(pmax, __shfl_xor(pmax, 32, kWave));
-      // the reference must be set (first used tile of a row) or raised (a score exceeds it
-      // by more than 2^8): rare, wave-uniform slow path
-      const bool need = row_any && (m_ref[m] == -INFINITY || !(pmax <= 256.f * vs));
+      lsum += __shfl_xor(lsum, 16, kWave);
+      lsum += __shfl_xor(lsum, 32, kWave);
+      // The reference must be set (first used tile of a row) or raised (a row sum passed
+      // 2^kRescaleLog2, or overflowed): rare, wave-uniform slow path.
+      const bool need = row_any && (m_ref[m] == -INFINITY || !(lsum * inv_vs <= 0x1p32f));
       if (__builtin_amdgcn_ballot_w64(need)) {
         float raw[8];
         scores(sel ? 0.f : -INFINITY, raw);
@@ -412,25 +423,24 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
         for (int k = 0; k < 8; ++k) mloc = fmaxf(mloc, raw[k]);
         mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-        const bool raise = row_any && (m_ref[m] == -INFINITY || mloc > m_ref[m] + kRescaleMargin);
-        const float m_new = raise ? mloc : m_ref[m];
+        const float m_new = need ? fmaxf(mloc, m_ref[m]) : m_ref[m];
         const float alpha = m_ref[m] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref[m] - m_new);
         l_run[m] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < C::kDt; ++dt) o[m][dt] *= alpha;
         m_ref[m] = m_new;
         const float bias = (sel && m_new != -INFINITY) ? lvs - m_new : -INFINITY;
+        lsum = 0.f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) pv[k] = __builtin_amdgcn_exp2f(raw[k] + bias);
+        for (int k = 0; k < 8; ++k) {
+          pv[k] = __builtin_amdgcn_exp2f(raw[k] + bias);
+          lsum += pv[k];
+        }
+        lsum += __shfl_xor(lsum, 16, kWave);
+        lsum += __shfl_xor(lsum, 32, kWave);
       }
-      float lsum = 0.f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        lsum += pv[k];
-        pf[m][k] = (__bf16)pv[k];
-      }
-      lsum += __shfl_xor(lsum, 16, kWave);
-      lsum += __shfl_xor(lsum, 32, kWave);
+      for (int k = 0; k < 8; ++k) pf[m][k] = (__bf16)pv[k];
       l_run[m] += lsum * inv_vs;
     }
 
@@ -499,16 +509,43 @@ pw_status launch_t(const Params& p, hipStream_t stream) {
 
 // Row tiling: <= 16 rows -> one wave, one row tile; <= 32 -> one wave, two row tiles;
 // <= 64 -> two waves of two row tiles.
+// Depth of the LDS tile ring.  The ring's LDS is what limits resident waves, and more
+// resident waves beat deeper prefetch: one-wave items use 2 stages (fp8 d=128: 16 KiB,
+// ten items per CU); items of 2 waves use 3, wider items 4.  PW_ATTN_STAGES (2, 3 or 4)
+// overrides it for tuning.
+template <int D, bool FP8, int MT, int NW>
+pw_status launch_nw(const Params& p, hipStream_t stream) {
+  static const int env_st = [] {
+    const char* e = getenv("PW_ATTN_STAGES");
+    const int v = e ? atoi(e) : 0;
+    return (v >= 2 && v <= 4) ? v : 0;
+  }();
+  const int st = env_st ? env_st : (NW == 1 ? 2 : (NW == 2 ? 3 : 4));
+  if (st == 2) return launch_t<D, FP8, MT, NW, 2>(p, stream);
+  if (st == 3) return launch_t<D, FP8, MT, NW, 3>(p, stream);
+  return launch_t<D, FP8, MT, NW, 4>(p, stream);
+}
+
+// Rows per work item: <= 16 -> one wave, one row tile; <= 32 -> one wave, two row tiles;
+// more -> 2, 4 or 8 waves of two row tiles sharing the LDS ring (the wide forms serve
+// shared per-KV-group tables, where every extra row reuses the staged tile).
 template <int D, bool FP8>
 pw_status launch_d(const Params& p, int rows, hipStream_t stream) {
-  constexpr int ST = FP8 ? 3 : 2;
-  if (rows <= 16) return launch_t<D, FP8, 1, 1, ST>(p, stream);
-  if (rows <= 32) return launch_t<D, FP8, 2, 1, ST>(p, stream);
-  if (rows <= 64) return launch_t<D, FP8, 2, 2, ST>(p, stream);
-  return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: %d rows per group", rows);
+  constexpr int kSlots = kTK * D * (FP8 ? 1 : 2) / 1024;    // 1 KiB load slots per tensor
+  if (rows <= 16) return launch_nw<D, FP8, 1, 1>(p, stream);
+  if (rows <= 32) return launch_nw<D, FP8, 2, 1>(p, stream);
+  if (rows <= 64) return launch_nw<D, FP8, 2, 2>(p, stream);
+  if constexpr (kSlots >= 4) if (rows <= 128) return launch_nw<D, FP8, 2, 4>(p, stream);
+  if constexpr (kSlots >= 8) if (rows <= 256) return launch_nw<D, FP8, 2, 8>(p, stream);
+  return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: %d rows per work item", rows);
 }
 
 }  // namespace
+
+int max_rows_per_item(int d, int kv_dtype) {
+  const int slots = kTK * d * (kv_dtype == PW_KV_FP8_E4M3 ? 1 : 2) / 1024;
+  return 32 * std::min(8, std::max(2, slots));
+}
 
 pw_status launch_sparse_prefill(const AttnArgs& a, hipStream_t stream) {
   Params p{};

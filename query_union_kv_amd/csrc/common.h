@@ -53,4 +53,7 @@ struct AttnArgs {
 
 pw_status launch_sparse_prefill(const AttnArgs& a, hipStream_t stream);
 
+// Largest (max_group * hq/hkv) one work item of pw_sparse_prefill supports.
+int max_rows_per_item(int d, int kv_dtype);
+
 }  // namespace pw

@@ -58,6 +58,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 // word the wave reads 64 consecutive flags (lane l <-> page 64w + l) and one ballot is the
 // word.  Flags are cleared as they are read, so the array is zero again for the next row.
 // Duplicate IDs write the same flag; negative IDs are skipped; IDs >= n_pages are counted.
+// MAXW > 0 bounds the word count at compile time, so every flag read of a row is issued
+// before the first ballot waits on it; MAXW == 0 is the general loop.
+template <int MAXW>
 __global__ void k_page_bitsets(const int32_t* __restrict__ topk, int n_rows, int hkv, int k,
                                int n_pages, int words, uint64_t* __restrict__ bits,
                                int32_t* __restrict__ bad_id_count) {
@@ -84,15 +87,31 @@ __global__ void k_page_bitsets(const int32_t* __restrict__ topk, int n_rows, int
     }
     wave_lds_sync();
     uint64_t* dst = bits + item * words;   // item = g * n_rows + r
-    uint64_t mine = 0;
-    for (int w = 0; w < words; ++w) {
-      const bool f = flags[w * kWave + lane] != 0;
-      const uint64_t word = __ballot(f);
-      flags[w * kWave + lane] = 0;
-      if (lane == (w & (kWave - 1))) mine = word;
-      if ((w & (kWave - 1)) == kWave - 1 || w == words - 1) {
-        const int base = w & ~(kWave - 1);
-        if (lane <= w - base) dst[base + lane] = mine;
+    if constexpr (MAXW > 0) {
+      uint8_t f[MAXW];
+#pragma unroll
+      for (int w = 0; w < MAXW; ++w) f[w] = w < words ? flags[w * kWave + lane] : 0;
+      uint64_t mine = 0;
+#pragma unroll
+      for (int w = 0; w < MAXW; ++w) {
+        const uint64_t word = __ballot(f[w] != 0);
+        if (lane == w) mine = word;
+      }
+#pragma unroll
+      for (int w = 0; w < MAXW; ++w)
+        if (w < words) flags[w * kWave + lane] = 0;
+      if (lane < words) dst[lane] = mine;
+    } else {
+      uint64_t mine = 0;
+      for (int w = 0; w < words; ++w) {
+        const bool f = flags[w * kWave + lane] != 0;
+        const uint64_t word = __ballot(f);
+        flags[w * kWave + lane] = 0;
+        if (lane == (w & (kWave - 1))) mine = word;
+        if ((w & (kWave - 1)) == kWave - 1 || w == words - 1) {
+          const int base = w & ~(kWave - 1);
+          if (lane <= w - base) dst[base + lane] = mine;
+        }
       }
     }
     wave_lds_sync();
@@ -236,10 +255,10 @@ __global__ __launch_bounds__(64) void k_group_wave(const uint64_t* __restrict__ 
     members[0] = seed;
     int cnt = 1;
     while (cnt < max_group && free_mask) {
-      int score = 0;
+      int score = 0;   // words past `words` are zero in every lane: no bound checks needed
 #pragma unroll
       for (int w = 0; w < MAXW; ++w)
-        if (w < words) score += __builtin_popcount(lo[w] & ulo[w]) + __builtin_popcount(hi[w] & uhi[w]);
+        score += __builtin_popcount(lo[w] & ulo[w]) + __builtin_popcount(hi[w] & uhi[w]);
       const bool is_free = (free_mask >> c) & 1ull;
       const int best = wave_max_dpp(is_free ? ((score << 6) | (63 - c)) : -1);
       const int pick = 63 - (best & 63);
@@ -384,9 +403,16 @@ pw_status launch_page_bitsets(const int32_t* topk, int n_rows, int hkv, int k, i
   const int waves = std::max(1, std::min(4, 65536 / per_wave));
   const int64_t want = (total + waves - 1) / waves;
   const int blocks = (int)std::min<int64_t>(want, 1024);
-  hipLaunchKernelGGL(k_page_bitsets, dim3(blocks), dim3(waves * kWave),
-                     (size_t)waves * per_wave, stream, topk, n_rows, hkv, k, n_pages, words, bits,
-                     bad_id_count);
+  const size_t lds = (size_t)waves * per_wave;
+  if (words <= 4)
+    hipLaunchKernelGGL(k_page_bitsets<4>, dim3(blocks), dim3(waves * kWave), lds, stream, topk,
+                       n_rows, hkv, k, n_pages, words, bits, bad_id_count);
+  else if (words <= 16)
+    hipLaunchKernelGGL(k_page_bitsets<16>, dim3(blocks), dim3(waves * kWave), lds, stream, topk,
+                       n_rows, hkv, k, n_pages, words, bits, bad_id_count);
+  else
+    hipLaunchKernelGGL(k_page_bitsets<0>, dim3(blocks), dim3(waves * kWave), lds, stream, topk,
+                       n_rows, hkv, k, n_pages, words, bits, bad_id_count);
   return check_launch("page_bitsets");
 }
 

@@ -34,6 +34,8 @@ def make_plan(w, grouping="affinity", window=None, max_group=None, dev="cuda"):
     c = w.cfg
     ids = w.topk if w.topk is not None else w.mask_rows
     mode = "topk" if w.topk is not None else "block_union"
+    if mode == "block_union" and max_group is None:
+        max_group = max(1, c.item_rows // c.g)
     return pw.SparsePrefill(nq=c.nq, hq=c.hq, hkv=c.hkv, d=c.d, n_pages=c.n_pages, page_size=c.ps,
                             kv_len=c.kv_len, k=ids.shape[2], window=window or c.window,
                             max_group=max_group or c.max_group, mode=mode, grouping=grouping,

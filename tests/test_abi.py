@@ -100,8 +100,12 @@ def _attn(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(d=96), -2), (dict(ps=32), -2), (dict(hq=6, hkv=4), -1), (dict(mg=9), -2),
-    (dict(hq=16, mg=8), -2),                       # G * max_group = 128 > 64
+    (dict(d=96), -2), (dict(ps=32), -2), (dict(hq=6, hkv=4), -1),
+    (dict(mg=9, gq=16, gs=16), -2),                # explicit groups hold <= 8 members
+    (dict(hq=16, mg=8, gq=16, gs=16), -2),         # G * max_group = 128 > 64 with groups
+    (dict(mg=300), -2),                            # consecutive wide groups: <= 256 members
+    (dict(hq=64, mg=8), -2),                       # 512 rows per work item > 256 (bf16, d=128)
+    (dict(hq=64, mg=4, kv_dtype=1, ks=16, vs=16), -2),  # fp8 d=128 wide items: <= 128 rows
     (dict(kv_dtype=2), -2), (dict(shared=2), -1), (dict(sp=100), -1),
     (dict(n_groups=0, nq=9), -1),                  # consecutive groups must cover nq
     (dict(sm=0.0), -1), (dict(nq=-1), -1),

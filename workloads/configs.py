@@ -34,6 +34,7 @@ class Config:
     pool_frac: float = 0.0  # block_union: fraction of prefix blocks in a KV group's pool
     window: int = 64        # grouping window W (consecutive query IDs)
     max_group: int = 8      # queries per group
+    item_rows: int = 128    # block_union: query-head rows per work item over a shared table
     seed: int = 1
 
     @property
