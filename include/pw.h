@@ -122,6 +122,20 @@ pw_status pw_union_tables(const uint64_t* bits, int n_rows, int hkv, int n_pages
                           int group_width, int k_max, int32_t* union_off, int32_t* union_pages,
                           uint8_t* union_qmask, int64_t capacity, hipStream_t stream);
 
+/* ---- (1)+(2)+(3) fused ------------------------------------------------------------------
+ * Exactly pw_page_bitsets(topk) followed by pw_group(bits) and
+ * pw_union_tables(bits, group_rows = group_qids, group_size, group_width = max_group,
+ * k_max = k, union_qmask): the same outputs, bit for bit, in fewer launches.  For
+ * window <= 64 and n_pages <= 1024 one workgroup per (window, KV head) builds the
+ * window's bitsets, groups it and sizes its unions (then a prefix sum and the union
+ * listing follow); other shapes run the three steps.  Arguments and limits as in the
+ * three calls; union_qmask is required; capacity >= pw_union_capacity(hkv*G,
+ * max_group, k, n_pages) with G = pw_num_groups(nq, window, max_group).            */
+pw_status pw_prepare(const int32_t* topk, int nq, int hkv, int k, int n_pages, int window,
+                     int max_group, uint64_t* bits, int32_t* bad_id_count, int32_t* group_qids,
+                     int32_t* group_size, int32_t* union_off, int32_t* union_pages,
+                     uint8_t* union_qmask, int64_t capacity, hipStream_t stream);
+
 /* ---- (4) ID-aware union attention -----------------------------------------------------
  * PageWeaver abstract, Fig. 1 and Fig. 3: each group's union pages are staged
  * on chip once; for every member the same lanes compute QK, the masked online

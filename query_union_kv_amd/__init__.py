@@ -22,7 +22,8 @@ import torch
 
 __all__ = [
     "PWError", "lib", "pw_version", "pw_words", "pw_num_groups", "pw_union_capacity",
-    "pw_page_bitsets", "pw_group", "pw_union_tables", "pw_sparse_prefill", "SparsePrefill",
+    "pw_page_bitsets", "pw_group", "pw_union_tables", "pw_prepare", "pw_sparse_prefill",
+    "SparsePrefill",
     "PW_KV_BF16", "PW_KV_FP8_E4M3", "LIB_PATH",
 ]
 
@@ -59,6 +60,7 @@ def lib() -> ctypes.CDLL:
             "pw_page_bitsets": (I, [P, I, I, I, I, P, P, P]),
             "pw_group": (I, [P, I, I, I, I, I, P, P, P]),
             "pw_union_tables": (I, [P, I, I, I, P, P, I, I, I, P, P, P, I64, P]),
+            "pw_prepare": (I, [P, I, I, I, I, I, I, P, P, P, P, P, P, P, I64, P]),
             "pw_sparse_prefill": (I, [P, I, I, I, I, P, P, I, P, P, I, I, I64, I64, P, I, F,
                                       P, P, I, I, I, P, P, P, I64, P, P, P]),
         }
@@ -152,6 +154,30 @@ def pw_union_tables(bits: torch.Tensor, n_pages: int, group_rows: torch.Tensor,
                                  union_pages.numel(), _stream(stream)))
 
 
+def pw_prepare(topk: torch.Tensor, n_pages: int, window: int, max_group: int,
+               bits: torch.Tensor, group_qids: torch.Tensor, group_size: torch.Tensor,
+               union_off: torch.Tensor, union_pages: torch.Tensor, union_qmask: torch.Tensor,
+               bad_id_count: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Fused pw_page_bitsets + pw_group + pw_union_tables (same outputs)."""
+    nq, hkv, k = topk.shape
+    n_groups = pw_num_groups(nq, window, max_group)
+    if tuple(bits.shape) != (hkv, nq, pw_words(n_pages)):
+        raise ValueError("bits shape")
+    if tuple(group_qids.shape) != (hkv, n_groups, max_group) or tuple(group_size.shape) != (hkv, n_groups):
+        raise ValueError("group_qids/group_size shapes do not match pw_num_groups")
+    if union_off.numel() != hkv * n_groups + 1 or union_qmask.numel() < union_pages.numel():
+        raise ValueError("union table buffer sizes")
+    _check(lib().pw_prepare(_ptr(topk, torch.int32, "topk"), nq, hkv, k, n_pages, window, max_group,
+                            _ptr(bits, torch.int64, "bits"),
+                            _ptr(bad_id_count, torch.int32, "bad_id_count"),
+                            _ptr(group_qids, torch.int32, "group_qids"),
+                            _ptr(group_size, torch.int32, "group_size"),
+                            _ptr(union_off, torch.int32, "union_off"),
+                            _ptr(union_pages, torch.int32, "union_pages"),
+                            _ptr(union_qmask, torch.uint8, "union_qmask"),
+                            union_pages.numel(), _stream(stream)))
+
+
 def pw_sparse_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                       q_pos: torch.Tensor, kv_len: int, union_off: torch.Tensor,
                       union_pages: torch.Tensor, out: torch.Tensor, *,
@@ -216,6 +242,7 @@ class SparsePrefill:
     mode: str = "topk"          # "topk" or "block_union"
     grouping: str = "affinity"  # "affinity" or "original" (topk mode)
     n_rows: int = 0             # block_union: mask rows per KV head
+    fused: bool = True          # topk/affinity mode: one pw_prepare call for the three steps
     device: str = "cuda"
 
     def __post_init__(self):
@@ -253,6 +280,11 @@ class SparsePrefill:
 
     def prepare(self, ids: torch.Tensor, stream=None) -> None:
         """Bitsets, grouping and union tables from topk [nq, hkv, k] or mask rows [n_rows, hkv, k]."""
+        if self.mode == "topk" and self.grouping == "affinity" and self.fused:
+            pw_prepare(ids, self.n_pages, self.window, self.max_group, self.bits, self.group_qids,
+                       self.group_size, self.union_off, self.union_pages, self.union_qmask,
+                       self.bad_ids, stream)
+            return
         pw_page_bitsets(ids, self.n_pages, self.bits, self.bad_ids, stream)
         if self.mode == "topk":
             if self.grouping == "affinity":

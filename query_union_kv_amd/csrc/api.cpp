@@ -125,6 +125,49 @@ pw_status pw_union_tables(const uint64_t* bits, int n_rows, int hkv, int n_pages
                                  stream);
 }
 
+pw_status pw_prepare(const int32_t* topk, int nq, int hkv, int k, int n_pages, int window,
+                     int max_group, uint64_t* bits, int32_t* bad_id_count, int32_t* group_qids,
+                     int32_t* group_size, int32_t* union_off, int32_t* union_pages,
+                     uint8_t* union_qmask, int64_t capacity, hipStream_t stream) {
+  pw::g_err[0] = 0;
+  if (nq < 0 || hkv < 1 || k < 1 || n_pages < 1)
+    return fail(PW_ERR_ARG, "pw_prepare: bad sizes nq=%d hkv=%d k=%d n_pages=%d", nq, hkv, k, n_pages);
+  if (k > 4096) return fail(PW_ERR_UNSUPPORTED, "pw_prepare: k=%d > 4096", k);
+  if (max_group < 1 || max_group > 8)
+    return fail(PW_ERR_UNSUPPORTED, "pw_prepare: max_group=%d not in 1..8", max_group);
+  if (window < 1 || window > 1024)
+    return fail(PW_ERR_UNSUPPORTED, "pw_prepare: window=%d not in 1..1024", window);
+  if (window % max_group)
+    return fail(PW_ERR_ARG, "pw_prepare: window=%d is not a multiple of max_group=%d", window,
+                max_group);
+  if (n_pages > 4096) return fail(PW_ERR_UNSUPPORTED, "pw_prepare: n_pages=%d > 4096", n_pages);
+  const int n_groups = pw_num_groups(nq, window, max_group);
+  if (n_groups < 0 || (int64_t)n_groups * hkv * max_group > INT32_MAX / 2)
+    return fail(PW_ERR_UNSUPPORTED, "pw_prepare: too many groups");
+  const int64_t need = pw_union_capacity(hkv * n_groups, max_group, k, n_pages);
+  if (capacity < need)
+    return fail(PW_ERR_CAPACITY, "pw_prepare: capacity %lld < required %lld", (long long)capacity,
+                (long long)need);
+  if (capacity > INT32_MAX)
+    return fail(PW_ERR_UNSUPPORTED, "pw_prepare: capacity %lld exceeds int32 offsets",
+                (long long)capacity);
+  if (!union_off) return fail(PW_ERR_ARG, "pw_prepare: null union_off");
+  if (nq > 0 && (!topk || !bits || !group_qids || !group_size || !union_pages || !union_qmask))
+    return fail(PW_ERR_ARG, "pw_prepare: null pointer argument");
+  if (pw::prepare_fusable(n_pages, window))
+    return pw::launch_prepare(topk, nq, hkv, k, n_pages, window, max_group, n_groups, bits,
+                              bad_id_count, group_qids, group_size, union_off, union_pages,
+                              union_qmask, capacity, stream);
+  pw_status st = pw::launch_page_bitsets(topk, nq, hkv, k, n_pages, bits, bad_id_count, stream);
+  if (st == PW_OK)
+    st = pw::launch_group(bits, nq, hkv, n_pages, window, max_group, n_groups, group_qids,
+                          group_size, stream);
+  if (st == PW_OK)
+    st = pw::launch_union_tables(bits, nq, hkv, n_pages, group_qids, group_size, n_groups,
+                                 max_group, union_off, union_pages, union_qmask, capacity, stream);
+  return st;
+}
+
 pw_status pw_sparse_prefill(const void* q, int nq, int hq, int hkv, int d, const void* k_cache,
                             const void* v_cache, int kv_dtype, const float* k_scale,
                             const float* v_scale, int page_size, int n_pages, int64_t stride_head,

@@ -27,6 +27,14 @@ pw_status launch_union_tables(const uint64_t* bits, int n_rows, int hkv, int n_p
                               int group_width, int32_t* union_off, int32_t* union_pages,
                               uint8_t* union_qmask, int64_t capacity, hipStream_t stream);
 
+// Fused bitsets + grouping + union tables (windows <= 64, n_pages <= 1024).
+bool prepare_fusable(int n_pages, int window);
+pw_status launch_prepare(const int32_t* topk, int nq, int hkv, int k, int n_pages, int window,
+                         int max_group, int n_groups, uint64_t* bits, int32_t* bad_id_count,
+                         int32_t* group_qids, int32_t* group_size, int32_t* union_off,
+                         int32_t* union_pages, uint8_t* union_qmask, int64_t capacity,
+                         hipStream_t stream);
+
 struct AttnArgs {
   const void* q;
   int nq, hq, hkv, d;

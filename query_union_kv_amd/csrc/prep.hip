@@ -284,6 +284,133 @@ __global__ __launch_bounds__(64) void k_group_wave(const uint64_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------------------
+// Fused preparation for windows of at most 64 queries and at most 1024 pages: one
+// workgroup per (window, KV head) builds the window's bitsets, runs the bounded greedy
+// grouping and writes every group's union size, so only the prefix sum and the union
+// listing remain.  Results are identical to the three separate steps.
+//  * bitsets: the window's rows live in LDS (64 x 1024 bits); every valid ID sets its bit
+//    with an LDS atomic OR, and the rows are copied out to `bits`;
+//  * grouping: wave v scores words [4v, 4v+4) of every candidate (lane = candidate) and the
+//    partial overlaps are summed through LDS, so the pick chain is split over up to four
+//    waves; the argmax key and the union U follow the single-wave search exactly.
+constexpr int kFusedWordsPerWave = 4;
+
+__global__ __launch_bounds__(256) void k_prepare(const int32_t* __restrict__ topk, int nq, int hkv,
+                                                 int k, int n_pages, int words, int window,
+                                                 int max_group, int n_groups,
+                                                 uint64_t* __restrict__ bits,
+                                                 int32_t* __restrict__ bad_id_count,
+                                                 int32_t* __restrict__ group_qids,
+                                                 int32_t* __restrict__ group_size,
+                                                 int32_t* __restrict__ union_count) {
+  __shared__ uint32_t rows[64][33];                    // +1 dword per row against bank conflicts
+  __shared__ int part[4][64];
+  __shared__ int red[4];
+  const int g = blockIdx.y;
+  const int start = blockIdx.x * window;
+  const int len = min(window, nq - start);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int nwaves = blockDim.x / kWave;
+
+  for (int i = tid; i < 64 * 33; i += blockDim.x) (&rows[0][0])[i] = 0u;
+  __syncthreads();
+  int bad = 0;
+  for (int idx = tid; idx < len * k; idx += blockDim.x) {
+    const int c = idx / k;
+    const int id = topk[((int64_t)(start + c) * hkv + g) * k + (idx - c * k)];
+    if (id >= n_pages) ++bad;
+    else if (id >= 0) atomicOr(&rows[c][id >> 5], 1u << (id & 31));
+  }
+  bad = wave_sum(bad);
+  if (bad_id_count != nullptr && lane == 0 && bad > 0) atomicAdd(bad_id_count, bad);
+  __syncthreads();
+  for (int idx = tid; idx < len * words; idx += blockDim.x) {
+    const int c = idx / words;
+    const int w = idx - c * words;
+    bits[((int64_t)g * nq + start + c) * words + w] =
+        (uint64_t)rows[c][2 * w] | ((uint64_t)rows[c][2 * w + 1] << 32);
+  }
+
+  // this wave's slice of the candidates' bitsets (zero past `words` and past `len`)
+  uint32_t lo[kFusedWordsPerWave], hi[kFusedWordsPerWave];
+#pragma unroll
+  for (int i = 0; i < kFusedWordsPerWave; ++i) {
+    const int w = wave * kFusedWordsPerWave + i;
+    const bool ok = lane < len && w < words;
+    lo[i] = ok ? rows[lane][2 * w] : 0u;
+    hi[i] = ok ? rows[lane][2 * w + 1] : 0u;
+  }
+  uint64_t free_mask = __ballot(lane < len);
+  const int64_t gbase = (int64_t)g * n_groups + (int64_t)blockIdx.x * (window / max_group);
+  int gi = 0;
+  while (free_mask) {
+    const int seed = __builtin_ctzll(free_mask);
+    free_mask &= free_mask - 1;
+    uint32_t ulo[kFusedWordsPerWave], uhi[kFusedWordsPerWave];
+#pragma unroll
+    for (int i = 0; i < kFusedWordsPerWave; ++i) {
+      ulo[i] = __builtin_amdgcn_readlane(lo[i], seed);
+      uhi[i] = __builtin_amdgcn_readlane(hi[i], seed);
+    }
+    int members[8];
+    members[0] = seed;
+    int cnt = 1;
+    while (cnt < max_group && free_mask) {
+      int partial = 0;
+#pragma unroll
+      for (int i = 0; i < kFusedWordsPerWave; ++i)
+        partial += __builtin_popcount(lo[i] & ulo[i]) + __builtin_popcount(hi[i] & uhi[i]);
+      int score = partial;
+      if (nwaves > 1) {
+        part[wave][lane] = partial;
+        __syncthreads();
+        score = 0;
+        for (int v = 0; v < nwaves; ++v) score += part[v][lane];
+      }
+      const bool is_free = (free_mask >> lane) & 1ull;
+      const int best = wave_max_dpp(is_free ? ((score << 6) | (63 - lane)) : -1);
+      const int pick = 63 - (best & 63);
+      free_mask &= ~(1ull << pick);
+#pragma unroll
+      for (int i = 0; i < kFusedWordsPerWave; ++i) {
+        ulo[i] |= __builtin_amdgcn_readlane(lo[i], pick);
+        uhi[i] |= __builtin_amdgcn_readlane(hi[i], pick);
+      }
+#pragma unroll
+      for (int j = 1; j < 8; ++j) if (j == cnt) members[j] = pick;
+      ++cnt;
+      if (nwaves > 1) __syncthreads();   // every wave has read `part` before it is rewritten
+    }
+    // union size: popcount of U over every wave's words
+    int usz = 0;
+#pragma unroll
+    for (int i = 0; i < kFusedWordsPerWave; ++i) usz += __builtin_popcount(ulo[i]) + __builtin_popcount(uhi[i]);
+    if (nwaves > 1) {
+      if (lane == 0) red[wave] = usz;
+      __syncthreads();
+      usz = 0;
+      for (int v = 0; v < nwaves; ++v) usz += red[v];
+      __syncthreads();
+    }
+    if (wave == 0) {
+      if (lane < max_group) {
+        int v = -1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) if (j == lane && j < cnt) v = start + members[j];
+        group_qids[(gbase + gi) * max_group + lane] = v;
+      }
+      if (lane == 0) {
+        group_size[gbase + gi] = cnt;
+        union_count[gbase + gi + 1] = usz;
+      }
+    }
+    ++gi;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // (3) union tables.  Table e = g * n_groups + j; one wave per table.
 __device__ __forceinline__ int member_count(const int32_t* group_size, int e, int group_width) {
   return group_size ? min(max(group_size[e], 0), group_width) : group_width;
@@ -312,8 +439,9 @@ __global__ void k_union_count(const uint64_t* __restrict__ bits, int n_rows, int
   if (lane == 0) union_off[e + 1] = cnt;
 }
 
-// In-place inclusive scan of union_off[1 .. n] by one workgroup of 1024 threads, so that
-// union_off becomes the exclusive prefix sum of the table sizes.
+// In-place inclusive scan of union_off[1 .. n] by one workgroup of 1024 threads (four
+// consecutive entries per thread per 4096-entry chunk), so that union_off becomes the
+// exclusive prefix sum of the table sizes.
 __global__ void k_union_scan(int32_t* __restrict__ union_off, int n) {
   __shared__ int wsum[16];
   __shared__ int carry_s;
@@ -323,17 +451,23 @@ __global__ void k_union_scan(int32_t* __restrict__ union_off, int n) {
     union_off[0] = 0;
   }
   __syncthreads();
-  for (int base = 0; base < n; base += 1024) {
-    const int i = base + t;
-    const int v = i < n ? union_off[i + 1] : 0;
-    const int ex = wave_excl_scan(v, lane);
-    if (lane == kWave - 1) wsum[wave] = ex + v;
+  for (int base = 0; base < n; base += 4096) {
+    const int i0 = base + 4 * t;
+    int v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = i0 + q < n ? union_off[i0 + q + 1] : 0;
+#pragma unroll
+    for (int q = 1; q < 4; ++q) v[q] += v[q - 1];
+    const int ex = wave_excl_scan(v[3], lane);
+    if (lane == kWave - 1) wsum[wave] = ex + v[3];
     __syncthreads();
     int before = carry_s;
     for (int k = 0; k < wave; ++k) before += wsum[k];
-    if (i < n) union_off[i + 1] = before + ex + v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (i0 + q < n) union_off[i0 + q + 1] = before + ex + v[q];
     __syncthreads();
-    if (t == 1023) carry_s = before + ex + v;
+    if (t == 1023) carry_s = before + ex + v[3];
     __syncthreads();
   }
 }
@@ -454,6 +588,34 @@ pw_status launch_group(const uint64_t* bits, int nq, int hkv, int n_pages, int w
   PW_GROUP_CASE(64)
 #undef PW_GROUP_CASE
   return fail(PW_ERR_UNSUPPORTED, "pw_group: n_pages=%d needs %d words > 64", n_pages, words);
+}
+
+bool prepare_fusable(int n_pages, int window) { return n_pages <= 1024 && window <= 64; }
+
+pw_status launch_prepare(const int32_t* topk, int nq, int hkv, int k, int n_pages, int window,
+                         int max_group, int n_groups, uint64_t* bits, int32_t* bad_id_count,
+                         int32_t* group_qids, int32_t* group_size, int32_t* union_off,
+                         int32_t* union_pages, uint8_t* union_qmask, int64_t capacity,
+                         hipStream_t stream) {
+  const int words = (n_pages + 63) / 64;
+  const int n_tables = hkv * n_groups;
+  if (nq > 0) {
+    const int nwaves = (words + kFusedWordsPerWave - 1) / kFusedWordsPerWave;
+    dim3 grid((nq + window - 1) / window, hkv), block(nwaves * kWave);
+    hipLaunchKernelGGL(k_prepare, grid, block, 0, stream, topk, nq, hkv, k, n_pages, words, window,
+                       max_group, n_groups, bits, bad_id_count, group_qids, group_size, union_off);
+    pw_status st = check_launch("prepare");
+    if (st != PW_OK) return st;
+  }
+  hipLaunchKernelGGL(k_union_scan, dim3(1), dim3(1024), 0, stream, union_off, n_tables);
+  pw_status st = check_launch("union_scan");
+  if (st != PW_OK || n_tables == 0) return st;
+  const int wpb = 4;
+  const int blocks = (n_tables + wpb - 1) / wpb;
+  hipLaunchKernelGGL(k_union_emit<true>, dim3(blocks), dim3(wpb * kWave), 0, stream, bits, nq,
+                     words, group_qids, group_size, n_groups, n_tables, max_group, union_off,
+                     union_pages, union_qmask, capacity);
+  return check_launch("union_emit");
 }
 
 pw_status launch_union_tables(const uint64_t* bits, int n_rows, int hkv, int n_pages,

@@ -30,7 +30,7 @@ def device_inputs(w, dev="cuda"):
     return d
 
 
-def make_plan(w, grouping="affinity", window=None, max_group=None, dev="cuda"):
+def make_plan(w, grouping="affinity", window=None, max_group=None, dev="cuda", fused=True):
     c = w.cfg
     ids = w.topk if w.topk is not None else w.mask_rows
     mode = "topk" if w.topk is not None else "block_union"
@@ -39,12 +39,13 @@ def make_plan(w, grouping="affinity", window=None, max_group=None, dev="cuda"):
     return pw.SparsePrefill(nq=c.nq, hq=c.hq, hkv=c.hkv, d=c.d, n_pages=c.n_pages, page_size=c.ps,
                             kv_len=c.kv_len, k=ids.shape[2], window=window or c.window,
                             max_group=max_group or c.max_group, mode=mode, grouping=grouping,
-                            n_rows=ids.shape[0] if mode == "block_union" else 0, device=dev)
+                            n_rows=ids.shape[0] if mode == "block_union" else 0, fused=fused,
+                            device=dev)
 
 
-def run_gpu(w, grouping="affinity", window=None, max_group=None, with_lse=True):
+def run_gpu(w, grouping="affinity", window=None, max_group=None, with_lse=True, fused=True):
     d = device_inputs(w)
-    plan = make_plan(w, grouping, window, max_group)
+    plan = make_plan(w, grouping, window, max_group, fused=fused)
     out = torch.full_like(d["q"], float("nan"))
     lse = torch.full(d["q"].shape[:2], float("nan"), dtype=torch.float32, device="cuda") if with_lse else None
     plan(d["ids"], d["q"], d["k"], d["v"], d["q_pos"], out, d["k_scale"], d["v_scale"], lse)

@@ -143,3 +143,28 @@ def test_run_to_run_determinism():
     b, _ = run_gpu(w)
     for k in ("out", "lse", "group_qids", "union_pages", "union_qmask"):
         assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
+FUSE_SHAPES = [
+    dict(nq=200, k=6, kv_len=2048),                                  # fused path
+    dict(nq=77, k=16, kv_len=4096, hq=8, hkv=2, window=32, max_group=4),
+    dict(nq=130, k=3, kv_len=65536, ps=64),                          # 1024 pages: last fused size
+    dict(nq=100, k=4, kv_len=70000),                                 # 1094 pages: three steps
+    dict(nq=300, k=8, kv_len=4096, window=128),                      # window > 64: three steps
+    dict(nq=9, k=64, kv_len=8192, max_group=1),
+]
+
+
+@pytest.mark.parametrize("kw", FUSE_SHAPES, ids=[",".join(f"{k}={v}" for k, v in s.items()) for s in FUSE_SHAPES])
+def test_fused_prepare_equals_separate_steps(kw):
+    """pw_prepare gives the same bitsets, groups and tables as the three separate calls,
+    and both equal the oracle."""
+    cfg = _small(**kw)
+    print(f"[parity] fused {kw}", flush=True)
+    w = make_workload(cfg)
+    w.topk = add_padding_and_duplicates(w.topk, seed=cfg.seed + 1)
+    a, _ = run_gpu(w, fused=True)
+    b, _ = run_gpu(w, fused=False)
+    for key in ("bits", "group_qids", "group_size", "union_off", "union_pages", "union_qmask", "out"):
+        assert np.array_equal(a[key], b[key]), key
+    _compare_tables(a, oracle_tables(w))
