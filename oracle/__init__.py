@@ -18,14 +18,17 @@ What it computes, in plain slow form (numpy fp64, pure-Python integer code):
                  same through group unions with member and causal masks
                  (route B: how the method reaches it), plus a pure-Python
                  brute force for tiny inputs.
+* ``kvcache``    writing a chunk's bf16 keys and values into the paged cache,
+                 with per-(KV head, page) fp8 e4m3fn quantisation.
 
 Pins (tests marked ``not gpu``): the Fig. 2 worked example, brute force on
 tiny inputs, dense equivalence with a library attention, closed forms,
-set-algebra identities, grouping invariance and the fp8/bf16 library casts.
+set-algebra identities, grouping invariance, the fp8/bf16 library casts, the
+e4m3fn format's error bound and the workload generator's own quantisation.
 The grouping rule's details beyond what Fig. 1/2 state (window, score, seed
 and tie-break) are readings, not pinned by the pages beyond Fig. 2: the
 heuristic's choices on the synthetic workloads are "parity unpinned" by the
 pages and are checked by invariants, hand traces and a brute-force argmax
 check instead.
 """
-from . import numerics, prep, attention  # noqa: F401
+from . import numerics, prep, attention, kvcache  # noqa: F401

@@ -11,9 +11,10 @@ import textwrap
 import pytest
 
 import test_oracle_attention as A
+import test_oracle_kvcache as K
 import test_oracle_numerics as N
 import test_oracle_prep as P
-from oracle import attention, numerics, prep
+from oracle import attention, kvcache, numerics, prep
 
 
 def _mutant(module, fn_name, old, new):
@@ -52,6 +53,16 @@ MUTATIONS = [
      lambda: P.test_fig2_printed_counts()),
     (prep, "union_tables", "qm |= 1 << j", "qm |= 1 << (len(members) - 1 - j)",
      lambda: P.test_union_tables_set_algebra()),
+    (kvcache, "e4m3fn_encode", "(hi % 2 == 0)", "(hi % 2 == 1)",
+     lambda: K.test_encode_ties_go_to_even_code()),
+    (kvcache, "quantize", "/ np.float32(scale)", "* np.float32(scale)",
+     lambda: K.test_full_append_matches_generator_quantisation()),
+    (kvcache, "_append_one", "s1 = min(last - base, ps - 1) + 1", "s1 = min(last - base, ps - 1)",
+     lambda: K.test_full_append_matches_generator_quantisation()),
+    (kvcache, "_append_one", "astype(np.float32) * s_old", "astype(np.float32) * s_new",
+     lambda: K.test_scale_growth_reencodes_earlier_slots()),
+    (kvcache, "_append_one", "if s_new > s_old:", "if s_new < s_old:",
+     lambda: K.test_scale_kept_when_chunk_is_smaller()),
 ]
 
 
