@@ -67,6 +67,38 @@ int pw_num_groups(int nq, int window, int max_group);
  * support size.  -1 on bad args. */
 int64_t pw_union_capacity(int n_tables, int group_width, int k_max, int n_pages);
 
+/* ---- (0) chunk K/V append ---------------------------------------------------------------
+ * PageWeaver abstract (FP8 KV throughout, chunked prefill) and CompactAttention
+ * "Approach" (attention in place over the paged, KV-head-major cache): the chunk's
+ * keys and values enter the cache before it is attended.  Token t = first_token + i
+ * goes to page t / page_size, slot t % page_size, of every KV head.
+ *   bf16 cache: the bits are copied.
+ *   fp8 cache, for K and V separately and every touched (KV head, page):
+ *     a = max |x| over the chunk's tokens on the page;
+ *     a page the chunk starts part way into (its earlier slots hold earlier tokens)
+ *     keeps its scale when a/448 does not exceed it, else takes a/448 and has its
+ *     earlier slots re-encoded from code * old scale; any other touched page takes
+ *     a/448, or 1 when a == 0.  Codes are e4m3fn(clamp(x / scale, -448, 448)) with
+ *     the correctly rounded fp32 quotient and round-to-nearest-even.
+ *   Slots after the chunk's last token on its last page are zeroed, so that every
+ *   slot of a page that attention reads holds a finite value.
+ * Pages other than the touched ones are not accessed.
+ *
+ * k_new, v_new  bf16, token i of KV head g at element i*stride_tok + g*d, the d
+ *               elements contiguous (e.g. slices of a fused QKV projection output)
+ * k_cache, v_cache, page_size, n_pages, stride_head, stride_page: as in
+ *               pw_sparse_prefill (elements of kv_dtype)
+ * k_scale, v_scale  fp32 [hkv][n_pages], read and written (fp8 only, else NULL)
+ * Non-finite inputs give unspecified codes (no fault).  Calls that overlap in time
+ * on the same pages race.
+ * Limits: n_tok >= 0, first_token >= 0, the chunk's last page < n_pages,
+ *   n_pages * page_size < 2^31, 8 <= d <= 1024 with d % 8 == 0, stride_tok >= hkv*d
+ *   and a multiple of 8, strides in bytes multiples of 16, pointers 16-byte aligned. */
+pw_status pw_append_kv(const void* k_new, const void* v_new, int n_tok, int hkv, int d,
+                       int64_t stride_tok, int first_token, void* k_cache, void* v_cache,
+                       int kv_dtype, float* k_scale, float* v_scale, int page_size, int n_pages,
+                       int64_t stride_head, int64_t stride_page, hipStream_t stream);
+
 /* ---- (1) page bitsets -------------------------------------------------------------
  * PageWeaver Fig. 1: fixed TopK pages per query guide the regrouping.  Row r of
  * KV head g becomes a bitset with bit p set iff page p is in the support, built

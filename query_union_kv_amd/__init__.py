@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "PWError", "lib", "pw_version", "pw_words", "pw_num_groups", "pw_union_capacity",
-    "pw_page_bitsets", "pw_group", "pw_union_tables", "pw_prepare", "pw_sparse_prefill",
+    "pw_append_kv", "pw_page_bitsets", "pw_group", "pw_union_tables", "pw_prepare", "pw_sparse_prefill",
     "SparsePrefill",
     "PW_KV_BF16", "PW_KV_FP8_E4M3", "LIB_PATH",
 ]
@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
             "pw_words": (I, [I]),
             "pw_num_groups": (I, [I, I, I]),
             "pw_union_capacity": (I64, [I, I, I, I]),
+            "pw_append_kv": (I, [P, P, I, I, I, I64, I, P, P, I, P, P, I, I, I64, I64, P]),
             "pw_page_bitsets": (I, [P, I, I, I, I, P, P, P]),
             "pw_group": (I, [P, I, I, I, I, I, P, P, P]),
             "pw_union_tables": (I, [P, I, I, I, P, P, I, I, I, P, P, P, I64, P]),
@@ -109,6 +110,51 @@ def pw_num_groups(nq: int, window: int, max_group: int) -> int:
 
 def pw_union_capacity(n_tables: int, group_width: int, k_max: int, n_pages: int) -> int:
     return lib().pw_union_capacity(n_tables, group_width, k_max, n_pages)
+
+
+def _token_rows(t: torch.Tensor, name: str):
+    """A bf16 [n_tok, hkv, d] view whose tokens may be strided (e.g. a slice of a fused
+    QKV output): returns (pointer, stride between tokens in elements)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != torch.bfloat16 or t.dim() != 3:
+        raise ValueError(f"{name} must be bf16 [n_tok, hkv, d]")
+    if t.numel() == 0:
+        return t.data_ptr(), t.shape[1] * t.shape[2]
+    if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{name}: heads and elements of a token must be contiguous")
+    return t.data_ptr(), (t.stride(0) if t.shape[0] > 1 else t.shape[1] * t.shape[2])
+
+
+def pw_append_kv(k_new: torch.Tensor, v_new: torch.Tensor, first_token: int,
+                 k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                 stream=None) -> None:
+    """Writes a chunk's bf16 keys/values [n_tok, hkv, d] at positions first_token.. into
+    the paged caches [hkv, n_pages, page_size, d] (bf16, or uint8 e4m3fn codes with fp32
+    scales [hkv, n_pages], which are updated)."""
+    n_tok, hkv, d = k_new.shape
+    if tuple(v_new.shape) != (n_tok, hkv, d):
+        raise ValueError("k_new and v_new shapes differ")
+    kp, ks_tok = _token_rows(k_new, "k_new")
+    vp, vs_tok = _token_rows(v_new, "v_new")
+    if ks_tok != vs_tok:
+        raise ValueError("k_new and v_new must share one token stride")
+    if k_cache.dim() != 4 or tuple(k_cache.shape) != tuple(v_cache.shape) or k_cache.shape[0] != hkv \
+            or k_cache.shape[3] != d:
+        raise ValueError("caches must be [hkv, n_pages, page_size, d]")
+    fp8 = k_cache.dtype == torch.uint8
+    dt = torch.uint8 if fp8 else torch.bfloat16
+    _, n_pages, ps, _ = k_cache.shape
+    if fp8 and (k_scale is None or v_scale is None or tuple(k_scale.shape) != (hkv, n_pages)
+                or tuple(v_scale.shape) != (hkv, n_pages)):
+        raise ValueError("fp8 caches need k_scale and v_scale [hkv, n_pages]")
+    _check(lib().pw_append_kv(kp, vp, n_tok, hkv, d, ks_tok, first_token,
+                              _ptr(k_cache, dt, "k_cache"), _ptr(v_cache, dt, "v_cache"),
+                              PW_KV_FP8_E4M3 if fp8 else PW_KV_BF16,
+                              _ptr(k_scale, torch.float32, "k_scale") if fp8 else None,
+                              _ptr(v_scale, torch.float32, "v_scale") if fp8 else None,
+                              ps, n_pages, n_pages * ps * d, ps * d, _stream(stream)))
 
 
 def pw_page_bitsets(topk: torch.Tensor, n_pages: int, bits: torch.Tensor,

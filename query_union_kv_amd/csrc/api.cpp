@@ -55,6 +55,45 @@ int64_t pw_union_capacity(int n_tables, int group_width, int k_max, int n_pages)
   return (int64_t)n_tables * per;
 }
 
+pw_status pw_append_kv(const void* k_new, const void* v_new, int n_tok, int hkv, int d,
+                       int64_t stride_tok, int first_token, void* k_cache, void* v_cache,
+                       int kv_dtype, float* k_scale, float* v_scale, int page_size, int n_pages,
+                       int64_t stride_head, int64_t stride_page, hipStream_t stream) {
+  pw::g_err[0] = 0;
+  if (n_tok < 0 || hkv < 1 || first_token < 0 || page_size < 1 || n_pages < 1)
+    return fail(PW_ERR_ARG, "pw_append_kv: bad sizes n_tok=%d hkv=%d first_token=%d page_size=%d n_pages=%d",
+                n_tok, hkv, first_token, page_size, n_pages);
+  if (d < 8 || d > 1024 || d % 8)
+    return fail(PW_ERR_UNSUPPORTED, "pw_append_kv: d=%d (a multiple of 8 in 8..1024)", d);
+  if (hkv > 65535) return fail(PW_ERR_UNSUPPORTED, "pw_append_kv: hkv=%d > 65535", hkv);
+  if ((int64_t)n_pages * page_size >= INT32_MAX)
+    return fail(PW_ERR_UNSUPPORTED, "pw_append_kv: n_pages*page_size must stay below 2^31");
+  if (kv_dtype != PW_KV_BF16 && kv_dtype != PW_KV_FP8_E4M3)
+    return fail(PW_ERR_UNSUPPORTED, "pw_append_kv: kv_dtype=%d", kv_dtype);
+  if (stride_tok < (int64_t)hkv * d || stride_tok % 8)
+    return fail(PW_ERR_ARG, "pw_append_kv: stride_tok=%lld must be >= hkv*d and a multiple of 8",
+                (long long)stride_tok);
+  const int esz = kv_dtype == PW_KV_FP8_E4M3 ? 1 : 2;
+  if (stride_page < (int64_t)page_size * d || stride_head < 0)
+    return fail(PW_ERR_ARG, "pw_append_kv: stride_page=%lld < page_size*d or stride_head < 0",
+                (long long)stride_page);
+  if ((stride_page * esz) % 16 || (stride_head * esz) % 16)
+    return fail(PW_ERR_ARG, "pw_append_kv: strides must be multiples of 16 bytes");
+  if (n_tok == 0) return PW_OK;
+  if ((int64_t)first_token + n_tok - 1 >= (int64_t)n_pages * page_size)
+    return fail(PW_ERR_CAPACITY, "pw_append_kv: tokens %d..%lld do not fit %d pages of %d",
+                first_token, (long long)first_token + n_tok - 1, n_pages, page_size);
+  if (!k_new || !v_new || !k_cache || !v_cache)
+    return fail(PW_ERR_ARG, "pw_append_kv: null required pointer");
+  if (kv_dtype == PW_KV_FP8_E4M3 && (!k_scale || !v_scale))
+    return fail(PW_ERR_ARG, "pw_append_kv: fp8 KV needs k_scale and v_scale");
+  if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_cache | (uintptr_t)v_cache) % 16)
+    return fail(PW_ERR_ARG, "pw_append_kv: inputs and caches must be 16-byte aligned");
+  return pw::launch_append_kv(k_new, v_new, n_tok, hkv, d, stride_tok, first_token, k_cache,
+                              v_cache, kv_dtype, k_scale, v_scale, page_size, n_pages, stride_head,
+                              stride_page, stream);
+}
+
 pw_status pw_page_bitsets(const int32_t* topk, int n_rows, int hkv, int k, int n_pages,
                           uint64_t* bits, int32_t* bad_id_count, hipStream_t stream) {
   pw::g_err[0] = 0;

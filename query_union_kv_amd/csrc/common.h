@@ -15,6 +15,12 @@ pw_status fail(pw_status status, const char* fmt, ...) __attribute__((format(pri
 pw_status check_launch(const char* what);
 
 // ---- launchers (validated arguments only) --------------------------------------------
+pw_status launch_append_kv(const void* k_new, const void* v_new, int n_tok, int hkv, int d,
+                           int64_t stride_tok, int first_token, void* k_cache, void* v_cache,
+                           int kv_dtype, float* k_scale, float* v_scale, int page_size,
+                           int n_pages, int64_t stride_head, int64_t stride_page,
+                           hipStream_t stream);
+
 pw_status launch_page_bitsets(const int32_t* topk, int n_rows, int hkv, int k, int n_pages,
                               uint64_t* bits, int32_t* bad_id_count, hipStream_t stream);
 

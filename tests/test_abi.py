@@ -139,3 +139,30 @@ def test_binding_rejects_host_tensors():
 def test_prepare_validation(args, code):
     st, msg = _err(L.pw_prepare(*args))
     assert st == code and msg.startswith("pw_prepare"), msg
+
+
+def _append(**kw):
+    a = dict(k_new=NULL, v_new=NULL, n_tok=10, hkv=2, d=128, stride_tok=256, first=0, kc=NULL,
+             vc=NULL, kv_dtype=0, ks=NULL, vs=NULL, ps=64, n_pages=4, sh=4 * 64 * 128,
+             sp=64 * 128, stream=NULL)
+    a.update(kw)
+    return _err(L.pw_append_kv(*a.values()))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=100), -2), (dict(d=0), -2), (dict(hkv=0), -1), (dict(n_tok=-1), -1),
+    (dict(first=-1), -1), (dict(kv_dtype=3), -2),
+    (dict(stride_tok=128), -1),                    # < hkv*d
+    (dict(stride_tok=260), -1),                    # not a multiple of 8 elements
+    (dict(sp=100), -1),                            # stride_page < page_size*d
+    (dict(first=250, n_tok=10), -3),               # tokens 250..259 past 4 pages of 64
+    (dict(), -1),                                  # null pointers
+    (dict(kv_dtype=1, k_new=16, v_new=16, kc=16, vc=16), -1),   # fp8 without scales
+])
+def test_append_validation(kw, code):
+    st, msg = _append(**kw)
+    assert st == code and msg.startswith("pw_append_kv"), msg
+
+
+def test_append_nothing_to_do_is_ok():
+    assert _append(n_tok=0)[0] == 0
