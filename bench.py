@@ -198,6 +198,17 @@ def main():
     ms_step = wall * 1e3 / args.steps
     value = cfg.nq / (ms_step / 1e3)
 
+    def timed(fn, n=10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
     # ---- structure of this call's tables --------------------------------------------------
     off = plan.union_off.cpu().numpy()
     total_pages = int(off[-1])
@@ -231,17 +242,6 @@ def main():
             "selected_edges": selected,
         })
 
-        def timed(fn, n=10):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            fn()
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(n):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / n
-
         # Fig. 6 / Eq. 7 decomposition: original-order Union call, attention over fixed
         # affinity tables, and the complete online affinity call.
         t_orig = timed(lambda: (orig.prepare(ids, stream),
@@ -260,6 +260,23 @@ def main():
     exec_flops = 4.0 * cfg.d * cfg.ps * exec_rows_pages
     extras["executed_tflops"] = exec_flops / (attn_ms / 1e3) / 1e12
     extras["attn_queries_per_s"] = cfg.nq / (attn_ms / 1e3)
+
+    # ---- the step before attention: appending the chunk's own keys and values -------------
+    # (into copies of the caches, so the attention inputs above stay as generated)
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+    kn = torch.randn((cfg.nq, cfg.hkv, cfg.d), generator=gen, device=dev).to(torch.bfloat16)
+    vn = torch.randn((cfg.nq, cfg.hkv, cfg.d), generator=gen, device=dev).to(torch.bfloat16)
+    kc2, vc2 = kc.clone(), vc.clone()
+    ks2, vs2 = (ks.clone(), vs.clone()) if ks is not None else (None, None)
+    t_app = timed(lambda: pw.pw_append_kv(kn, vn, cfg.first_pos, kc2, vc2, ks2, vs2, stream=stream))
+    esize = 1 if cfg.kv_dtype == "fp8" else 2
+    n_app_pages = (cfg.kv_len - 1) // cfg.ps - cfg.first_pos // cfg.ps + 1
+    app_bytes = 2 * cfg.nq * cfg.hkv * cfg.d * 2 + 2 * n_app_pages * cfg.hkv * cfg.ps * cfg.d * esize
+    if esize == 1:
+        app_bytes += 2 * n_app_pages * cfg.hkv * 4
+    extras["append_kv"] = {"ms": t_app, "bytes": app_bytes, "GBs": app_bytes / (t_app / 1e3) / 1e9,
+                           "hbm_frac": app_bytes / (t_app / 1e3) / 1e9 / HBM_PEAK_GBS}
+    del kc2, vc2, ks2, vs2
 
     # ---- flushed timing: 512 MiB written before each step, outside the event pair ----------
     if args.flush_steps:

@@ -6,6 +6,7 @@ import torch
 
 import query_union_kv_amd as pw
 from oracle import kvcache
+from oracle.numerics import E4M3FN_TABLE
 
 pytestmark = pytest.mark.gpu
 
@@ -96,7 +97,7 @@ def test_append_parity(dtype, first, n_tok):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-@pytest.mark.parametrize("ps,d", [(64, 64), (128, 128), (16, 8), (64, 136)])
+@pytest.mark.parametrize("ps,d", [(64, 64), (128, 128), (16, 8), (64, 136), (256, 128)])
 def test_append_sequence_of_chunks(dtype, ps, d):
     """Chunked prefill: consecutive ragged chunks, magnitudes varying so that some
     pages keep and some grow their scales; a strided (fused QKV) source."""
@@ -122,6 +123,28 @@ def test_append_full_size_chunk(dtype):
     state = _initial_cache(rng, hkv, n_pages, ps, d, dtype)
     _run_both(state, [(kv_len - n_tok, _chunk(rng, n_tok, hkv, d, 1.0), _chunk(rng, n_tok, hkv, d, 3.0))],
               ps, dtype)
+
+
+@pytest.mark.parametrize("scale", [0.125, 0.3, 2.0 ** -20])
+def test_append_rounding_ties(scale):
+    """Values at, and one bf16 step either side of, every e4m3fn rounding midpoint times
+    the page scale (exact ties when the scale is a power of two), appended part way
+    into a page whose scale they do not raise."""
+    fin = E4M3FN_TABLE[:0x7F]
+    mids = ((fin[1:] + fin[:-1]) / 2 * np.float32(scale)).astype(np.float32)
+    b = _bf16_bits(mids).astype(np.int32)
+    vals = np.concatenate([b, b - 1, b + 1]).astype(np.uint16)
+    vals = np.concatenate([vals, vals | 0x8000])
+    hkv, n_pages, ps, d = 1, 2, 64, 128
+    n_tok = -(-vals.size // d)
+    chunk = np.zeros(n_tok * d, np.uint16)
+    chunk[:vals.size] = vals
+    chunk = chunk.reshape(n_tok, hkv, d)
+    rng = np.random.default_rng(3)
+    k, v, ks, vs = _initial_cache(rng, hkv, n_pages, ps, d, "fp8")
+    ks[:] = np.float32(scale)
+    vs[:] = np.float32(scale)
+    _run_both((k, v, ks, vs), [(5, chunk, chunk[::-1].copy())], ps, "fp8")
 
 
 def test_append_nothing_is_a_noop():
