@@ -22,10 +22,11 @@
 //     ends with one query row and 8 of its keys and row statistics stay in
 //     the lane;
 //   * support mask (the member selected the page) + causal mask, online
-//     softmax in the log2 domain; the running maximum used for the
-//     exponentials is only raised when a row's maximum exceeds it by more
-//     than 2^8, so the accumulators are rescaled rarely (exact either way:
-//     numerator and denominator share the reference);
+//     softmax in the log2 domain; the reference used for the exponentials
+//     is set on a row's first used tile and raised only when a tile's row
+//     sum of P = 2^(score - reference) passes 2^32, so the accumulators are
+//     rescaled rarely (exact either way: numerator and denominator share
+//     the reference);
 //   * O^T[d][row] += V^T . P^T on MFMA, V^T read from LDS with the CDNA4
 //     transposing loads (ds_read_b64_tr_b8 / _b16).
 // fp8 (OCP e4m3fn) codes are converted exactly to bf16; the K page scale folds
