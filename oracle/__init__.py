@@ -11,13 +11,15 @@ What it computes, in plain slow form (numpy fp64, pure-Python integer code):
 * ``numerics``   bf16 and OCP fp8-e4m3fn decoding from their definitions.
 * ``prep``       per-(query, KV head) page bitsets, the bounded greedy
                  affinity grouping, per-group page-union tables with member
-                 masks, and the page-visit / masked-slot statistics of
-                 PageWeaver Fig. 2 and Fig. 6.
+                 masks, the page-visit / masked-slot statistics of
+                 PageWeaver Fig. 2 and Fig. 6, and the page-major work items
+                 of the direct KV-page union.
 * ``attention``  causal softmax attention of every query over exactly its
-                 own pages (route A: per-query gather, the definition) and the
+                 own pages (route A: per-query gather, the definition), the
                  same through group unions with member and causal masks
-                 (route B: how the method reaches it), plus a pure-Python
-                 brute force for tiny inputs.
+                 (route B: how the method reaches it) and through the direct
+                 KV-page union with per-page partials merged by lse (route C),
+                 plus a pure-Python brute force for tiny inputs.
 * ``kvcache``    writing a chunk's bf16 keys and values into the paged cache,
                  with per-(KV head, page) fp8 e4m3fn quantisation.
 

@@ -102,6 +102,49 @@ def route_b(q_bits, k_data, v_data, k_scale, v_scale, kv_dtype: str,
     return O, L
 
 
+def route_c(q_bits, k_data, v_data, k_scale, v_scale, kv_dtype: str,
+            S: List[List[frozenset]], q_pos, kv_len: int, ps: int, sm_scale: float):
+    """Through the direct KV-page union (PageWeaver abstract, its complementary
+    page-major study): every (KV head, page) is visited once for all queries that
+    selected it; each (query, head, page) gives a partial softmax over that page's
+    usable keys - a normalised output o_i and its lse_i - and each row's partials
+    are merged by their lse:  lse = log sum_i exp(lse_i),
+    O = sum_i exp(lse_i - lse) o_i  (empty rows: O = 0, lse = -inf).
+    Returns O fp64 [nq, hq, d], lse [nq, hq]."""
+    nq, hq, d = q_bits.shape
+    hkv = k_data.shape[0]
+    G = hq // hkv
+    n_pages = k_data.shape[1]
+    parts = {}
+    for g in range(hkv):
+        Kg = decode_kv(k_data[g], None if k_scale is None else k_scale[g], kv_dtype)
+        Vg = decode_kv(v_data[g], None if v_scale is None else v_scale[g], kv_dtype)
+        lists = [[] for _ in range(n_pages)]
+        for i in range(nq):
+            for p in sorted(S[g][i]):
+                lists[p].append(i)
+        for p in range(n_pages):
+            t = p * ps + np.arange(ps)
+            for i in lists[p]:
+                keep = (t <= int(q_pos[i])) & (t < kv_len)
+                qh = bf16_bits_to_f64(q_bits[i, g * G:(g + 1) * G])
+                o, lse = _softmax_pv(sm_scale * (qh @ Kg[p][keep].T), Vg[p][keep])
+                parts.setdefault((i, g), []).append((lse, o))
+    O = np.zeros((nq, hq, d))
+    L = np.full((nq, hq), -np.inf)
+    for (i, g), lst in parts.items():
+        lses = np.stack([x[0] for x in lst])            # [n_parts, G]
+        outs = np.stack([x[1] for x in lst])            # [n_parts, G, d]
+        m = lses.max(axis=0)
+        ok = np.isfinite(m)
+        w = np.where(ok[None, :], np.exp(lses - np.where(ok, m, 0.0)[None, :]), 0.0)
+        tot = w.sum(axis=0)
+        O[i, g * G:(g + 1) * G] = np.where(ok[:, None], (w[:, :, None] * outs).sum(axis=0)
+                                           / np.where(ok, tot, 1.0)[:, None], 0.0)
+        L[i, g * G:(g + 1) * G] = np.where(ok, m + np.log(np.where(ok, tot, 1.0)), -np.inf)
+    return O, L
+
+
 def brute_force(q_bits, k_data, v_data, k_scale, v_scale, kv_dtype: str,
                 S: List[List[frozenset]], q_pos, kv_len: int, ps: int, sm_scale: float):
     """Explicit scalar loops with math.exp over every (query, head, token): tiny inputs only."""

@@ -190,3 +190,61 @@ def block_tables(mask_rows: np.ndarray, n_pages: int) -> List[List[int]]:
     (all Q-blocks x all heads of the group) of each KV head, ascending."""
     S = supports(mask_rows, n_pages)
     return [sorted(frozenset().union(*rows)) for rows in S]
+
+
+# ---------------------------------------------------------------------------
+# page-major tables (direct KV-page union)
+
+
+def page_lists(bits_g: Sequence[int], n_pages: int) -> List[List[int]]:
+    """For one KV head: for every page P, the ascending IDs of the queries whose
+    support holds P.  This is the page-major view of the same supports that
+    PageWeaver's direct KV-page union visits once per page (abstract)."""
+    lists: List[List[int]] = [[] for _ in range(n_pages)]
+    for q, b in enumerate(bits_g):
+        p = 0
+        while b:
+            if b & 1:
+                lists[p].append(q)
+            b >>= 1
+            p += 1
+    return lists
+
+
+def support_rank(b: int, page: int) -> int:
+    """Position of ``page`` among the ascending pages of the support bitset b."""
+    return bin(b & ((1 << page) - 1)).count("1")
+
+
+def page_items(bits: List[List[int]], n_pages: int, chunk: int, k_max: int):
+    """Work items of the page-major execution, ordered by KV head, then page, then
+    position in the page's query list: each item is (g, P, members, slots), where
+    members are up to ``chunk`` consecutive IDs of P's list and member q's partial
+    result goes to slot (q * hkv + g) * k_max + (rank of P in S(q, g))."""
+    hkv = len(bits)
+    items = []
+    for g, bits_g in enumerate(bits):
+        lists = page_lists(bits_g, n_pages)
+        for p in range(n_pages):
+            qs = lists[p]
+            for c in range(0, len(qs), chunk):
+                members = qs[c:c + chunk]
+                slots = [(q * hkv + g) * k_max + support_rank(bits_g[q], p) for q in members]
+                items.append((g, p, members, slots))
+    return items
+
+
+def page_items_to_arrays(items, chunk: int):
+    """item_kvh int32 [n], union_pages int32 [n] (the item's page), group_qids and
+    out_slot int32 [n, chunk] (-1 padded), group_size int32 [n]."""
+    n = len(items)
+    kvh = np.array([it[0] for it in items], dtype=np.int32)
+    pages = np.array([it[1] for it in items], dtype=np.int32)
+    qids = np.full((n, chunk), -1, dtype=np.int32)
+    slots = np.full((n, chunk), -1, dtype=np.int32)
+    size = np.zeros(n, dtype=np.int32)
+    for i, (_, _, members, sl) in enumerate(items):
+        qids[i, :len(members)] = members
+        slots[i, :len(sl)] = sl
+        size[i] = len(members)
+    return kvh, pages, qids, slots, size

@@ -180,3 +180,24 @@ def test_nrms_definition():
     ref = np.array([3.0, 4.0])
     assert attention.nrms(ref, ref) == 0.0
     assert attention.nrms(np.array([3.0, 4.5]), ref) == pytest.approx(10.0)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_direct_page_union_route_c_equals_definition(kv_dtype):
+    """The direct KV-page union (partials per (query, page), merged by their lse)
+    reaches the definition, including empty supports, pages wholly in a query's
+    future and positions past the cache end."""
+    w = tiny_workload(kv_dtype=kv_dtype, hq=4, hkv=2, d=16, ps=8, kv_len=197, nq=40, k=5, seed=14)
+    c = w.cfg
+    topk = add_padding_and_duplicates(w.topk, 3)
+    topk[0, 0, :] = -1                                        # an empty support
+    topk[1, 1, 0] = c.n_pages - 1                             # a page after the query
+    S = prep.supports(topk, c.n_pages)
+    OA, LA = _route_a(w, S)
+    OC, LC = attention.route_c(w.q, w.k, w.v, w.k_scale, w.v_scale, kv_dtype, S, w.q_pos,
+                               c.kv_len, c.ps, 1.0 / math.sqrt(c.d))
+    assert np.allclose(OC, OA, rtol=0, atol=1e-12)
+    assert (np.isneginf(LC) == np.isneginf(LA)).all()
+    fin = np.isfinite(LA)
+    assert np.allclose(LC[fin], LA[fin], rtol=0, atol=1e-12)
+    assert np.isneginf(LC[0, :2]).all() and not OC[0, :2].any()

@@ -53,6 +53,14 @@ MUTATIONS = [
      lambda: P.test_fig2_printed_counts()),
     (prep, "union_tables", "qm |= 1 << j", "qm |= 1 << (len(members) - 1 - j)",
      lambda: P.test_union_tables_set_algebra()),
+    (attention, "route_c", "(w[:, :, None] * outs).sum(axis=0)", "outs.sum(axis=0)",
+     lambda: A.test_direct_page_union_route_c_equals_definition("bf16")),
+    (attention, "route_c", "keep = (t <= int(q_pos[i])) & (t < kv_len)", "keep = (t < kv_len)",
+     lambda: A.test_direct_page_union_route_c_equals_definition("fp8")),
+    (prep, "page_items", "support_rank(bits_g[q], p)", "support_rank(bits_g[q], p + 1)",
+     lambda: P.test_page_items_hand_trace()),
+    (prep, "page_items", "range(0, len(qs), chunk)", "range(0, len(qs), chunk + 1)",
+     lambda: P.test_page_items_cover_every_edge_once()),
     (kvcache, "e4m3fn_encode", "(hi % 2 == 0)", "(hi % 2 == 1)",
      lambda: K.test_encode_ties_go_to_even_code()),
     (kvcache, "quantize", "/ np.float32(scale)", "* np.float32(scale)",

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 from oracle import prep
+from helpers import tiny_workload
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -183,3 +184,40 @@ def test_stats_definitions():
 def test_block_tables_union():
     rows = np.array([[[0, 3, -1]], [[3, 7, 9]], [[-1, -1, 2]]], dtype=np.int32)
     assert prep.block_tables(rows, 10) == [[0, 2, 3, 7, 9]]
+
+
+def test_page_lists_hand_trace():
+    # query 0: pages {0, 2}; query 1: {2}; query 2: {}; query 3: {0, 1, 2}
+    bits = [0b101, 0b100, 0, 0b111]
+    assert prep.page_lists(bits, 4) == [[0, 3], [3], [0, 1, 3], []]
+    assert [prep.support_rank(0b111, p) for p in range(3)] == [0, 1, 2]
+    assert prep.support_rank(0b101, 2) == 1
+
+
+def test_page_items_hand_trace():
+    bits = [[0b101, 0b100, 0, 0b111], [0b10, 0, 0, 0]]     # two KV heads, 4 queries
+    items = prep.page_items(bits, 4, chunk=2, k_max=3)
+    # head 0: page 0 -> [0, 3]; page 1 -> [3]; page 2 -> [0, 1] and [3]; head 1: page 1 -> [0]
+    assert [(g, p, m) for g, p, m, _ in items] == [
+        (0, 0, [0, 3]), (0, 1, [3]), (0, 2, [0, 1]), (0, 2, [3]), (1, 1, [0])]
+    # slot = (q * hkv + g) * k_max + rank
+    assert [s for *_, s in items] == [[0, 18], [19], [1, 6], [20], [3]]
+
+
+def test_page_items_cover_every_edge_once():
+    w = tiny_workload(hq=4, hkv=2, ps=4, kv_len=120, nq=33, k=6, seed=21)
+    c = w.cfg
+    bits = prep.page_bitsets(w.topk, c.n_pages)
+    S = prep.supports(w.topk, c.n_pages)
+    k_max = w.topk.shape[2]
+    for chunk in (1, 3, 8):
+        items = prep.page_items(bits, c.n_pages, chunk, k_max)
+        edges = [(g, q, p) for g, p, members, _ in items for q in members]
+        assert len(edges) == len(set(edges)) == sum(len(s) for Sg in S for s in Sg)
+        assert set(edges) == {(g, q, p) for g in range(c.hkv) for q in range(c.nq) for p in S[g][q]}
+        slots = [s for *_, sl in items for s in sl]
+        assert len(set(slots)) == len(slots) and max(slots) < c.nq * c.hkv * k_max
+        for g, p, members, sl in items:
+            assert 1 <= len(members) <= chunk and members == sorted(members)
+            for q, s in zip(members, sl):
+                assert s == (q * c.hkv + g) * k_max + sorted(S[g][q]).index(p)
