@@ -254,6 +254,25 @@ def main():
                              "execution_saving": t_orig_attn - t_fixed,
                              "online_cost": t_online - t_fixed, "net_saving": t_orig - t_online}
         exec_rows_pages = float((sizes * gsz).sum()) * cfg.g     # (row, union page) pairs
+
+        # The direct KV-page union on the same inputs: every (KV head, page) once,
+        # per-page partials, lse merge (a separate entry point, compared here).
+        pu = pw.PageUnionPrefill(nq=cfg.nq, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, n_pages=cfg.n_pages,
+                                 page_size=cfg.ps, kv_len=cfg.kv_len, k=ids.shape[2], device=dev)
+        out_pu = torch.empty_like(q)
+        t_pu_prep = timed(lambda: pu.prepare(ids, stream))
+        t_pu_attn = timed(lambda: pu.attend(q, kc, vc, q_pos, out_pu, ks, vs, stream=stream))
+        t_pu_call = timed(lambda: pu(ids, q, kc, vc, q_pos, out_pu, ks, vs, stream=stream))
+        n_items = pu.n_items
+        distinct = int((np.diff(pu.item_off.cpu().numpy()) > 0).sum())  # (KV head, page) pairs used
+        page_bytes = cfg.ps * cfg.d * (1 if cfg.kv_dtype == "fp8" else 2) * 2 + (8 if cfg.kv_dtype == "fp8" else 0)
+        partial_bytes = 2 * selected * cfg.g * (cfg.d * 2 + 4)          # written, then read by the merge
+        extras["direct_page_union"] = {
+            "call_ms": t_pu_call, "prep_ms": t_pu_prep, "attn_and_merge_ms": t_pu_attn,
+            "queries_per_s": cfg.nq / (t_pu_call / 1e3), "items": n_items,
+            "distinct_kv_bytes": distinct * page_bytes, "partial_bytes": partial_bytes,
+            "max_abs_vs_union": float((out_pu.float() - out.float()).abs().max().item())}
+        del pu, out_pu
     else:
         exec_rows_pages = float(visits) * max_group * cfg.g      # item rows x its table pages
     # executed MFMA work: QK and PV, 2 flops per MAC, over every (row, union token)

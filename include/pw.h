@@ -217,6 +217,62 @@ pw_status pw_sparse_prefill(const void* q, int nq, int hq, int hkv, int d,
                             const int32_t* union_pages, const uint8_t* union_qmask,
                             int64_t capacity, void* out, float* lse, hipStream_t stream);
 
+/* ---- (5) direct KV-page union (page-major execution) -----------------------------------
+ * PageWeaver abstract: the page-major alternative to query unions visits every
+ * (KV head, page) once for all queries that selected it, and pays for it with
+ * per-page partial results that must be reduced.  Work item = (KV head g, page P,
+ * up to `chunk` consecutive queries of P's ascending list of selecting queries).
+ * Every member's partial result - the causal softmax over P's usable keys,
+ * normalised, with its lse - goes to slot (q*hkv + g)*k_max + rank, rank = the
+ * position of P among the ascending pages of S(q, g); each row's partials are then
+ * merged by their lse.  The result is the same attention as pw_sparse_prefill over
+ * the same supports.
+ *
+ * Upper bound on the items pw_page_tables writes: min(E, ceil((E + hkv*n_pages*(chunk-1))
+ * / chunk)) with E = nq*hkv*min(k_max, n_pages).  -1 on bad args.                      */
+int64_t pw_page_items_capacity(int nq, int hkv, int k_max, int n_pages, int chunk);
+
+/* Bytes of workspace pw_page_tables needs: the per-page query columns
+ * (hkv*n_pages*ceil(nq/64) uint64) and a per-row rank table (hkv*nq*pw_words(n_pages)
+ * int32).  0 on bad args.                                                                */
+size_t pw_page_workspace_bytes(int nq, int hkv, int n_pages);
+
+/* Page-major work items from support bitsets.
+ * bits        uint64 [hkv][nq][pw_words(n_pages)] (from pw_page_bitsets)
+ * k_max       bounds every support size (the TopK width); partial slots use it
+ * workspace   device buffer of workspace_bytes >= pw_page_workspace_bytes(), 8-byte aligned
+ * item_off    int32 [hkv*n_pages + 1] output: exclusive prefix sum of items per (g, P),
+ *             KV-head-major; item_off[hkv*n_pages] = number of items N
+ * item_kvh, item_page, item_size  int32 [item_capacity] outputs (first N written)
+ * item_qids, item_slot  int32 [item_capacity][chunk] outputs: members (ascending IDs)
+ *             and their partial slots, -1 padded
+ * Limits: 1 <= chunk <= 64, n_pages <= 65536, nq*hkv*k_max < 2^31,
+ *   item_capacity >= pw_page_items_capacity(...).                                        */
+pw_status pw_page_tables(const uint64_t* bits, int nq, int hkv, int n_pages, int k_max, int chunk,
+                         void* workspace, size_t workspace_bytes, int32_t* item_off,
+                         int32_t* item_kvh, int32_t* item_page, int32_t* item_qids,
+                         int32_t* item_size, int32_t* item_slot, int64_t item_capacity,
+                         hipStream_t stream);
+
+/* Attention through page-major items, then the lse merge.  Arguments q .. sm_scale,
+ * out and lse as in pw_sparse_prefill (every row of out/lse is written); bits, k_max,
+ * chunk and the item arrays as given to / written by pw_page_tables.
+ * partial_o    workspace bf16 [nq*hkv*k_max*(hq/hkv)][d]: normalised partial rows
+ * partial_lse  workspace fp32 [nq*hkv*k_max*(hq/hkv)]
+ * Limits: d in {64, 128}; page_size in {64, 128}; 1 <= chunk <= 64 and
+ *   (hq/hkv)*chunk <= 256 rows (bf16, d=128), 128 (fp8 d=128, bf16 d=64), 64 (fp8 d=64);
+ *   k_max*(hq/hkv) <= 16384.                                                              */
+pw_status pw_page_union_prefill(const void* q, int nq, int hq, int hkv, int d, const void* k_cache,
+                                const void* v_cache, int kv_dtype, const float* k_scale,
+                                const float* v_scale, int page_size, int n_pages,
+                                int64_t stride_head, int64_t stride_page, const int32_t* q_pos,
+                                int kv_len, float sm_scale, const uint64_t* bits, int k_max,
+                                int chunk, const int32_t* item_off, const int32_t* item_kvh,
+                                const int32_t* item_page, const int32_t* item_qids,
+                                const int32_t* item_size, const int32_t* item_slot,
+                                int64_t item_capacity, void* partial_o, float* partial_lse,
+                                void* out, float* lse, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,6 +64,11 @@ def lib() -> ctypes.CDLL:
             "pw_prepare": (I, [P, I, I, I, I, I, I, P, P, P, P, P, P, P, I64, P]),
             "pw_sparse_prefill": (I, [P, I, I, I, I, P, P, I, P, P, I, I, I64, I64, P, I, F,
                                       P, P, I, I, I, P, P, P, I64, P, P, P]),
+            "pw_page_items_capacity": (I64, [I, I, I, I, I]),
+            "pw_page_workspace_bytes": (ctypes.c_size_t, [I, I, I]),
+            "pw_page_tables": (I, [P, I, I, I, I, I, P, ctypes.c_size_t, P, P, P, P, P, P, I64, P]),
+            "pw_page_union_prefill": (I, [P, I, I, I, I, P, P, I, P, P, I, I, I64, I64, P, I, F,
+                                          P, I, I, P, P, P, P, P, P, I64, P, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -260,6 +265,130 @@ def pw_sparse_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _ptr(union_pages, torch.int32, "union_pages"), _ptr(union_qmask, torch.uint8, "union_qmask"),
         union_pages.numel(), _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"),
         _stream(stream)))
+
+
+def _cache_dtype(k_cache: torch.Tensor) -> int:
+    if k_cache.dtype == torch.bfloat16:
+        return PW_KV_BF16
+    if k_cache.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PW_KV_FP8_E4M3
+    raise ValueError(f"unsupported cache dtype {k_cache.dtype}")
+
+
+def pw_page_items_capacity(nq: int, hkv: int, k_max: int, n_pages: int, chunk: int) -> int:
+    return lib().pw_page_items_capacity(nq, hkv, k_max, n_pages, chunk)
+
+
+def pw_page_workspace_bytes(nq: int, hkv: int, n_pages: int) -> int:
+    return lib().pw_page_workspace_bytes(nq, hkv, n_pages)
+
+
+def pw_page_tables(bits: torch.Tensor, n_pages: int, k_max: int, chunk: int, workspace: torch.Tensor,
+                   item_off: torch.Tensor, item_kvh: torch.Tensor, item_page: torch.Tensor,
+                   item_qids: torch.Tensor, item_size: torch.Tensor, item_slot: torch.Tensor,
+                   stream=None) -> None:
+    """Page-major work items of the direct KV-page union from bits [hkv, nq, words]."""
+    hkv, nq, _ = bits.shape
+    cap = item_kvh.numel()
+    if item_off.numel() != hkv * n_pages + 1:
+        raise ValueError("item_off size")
+    if item_page.numel() != cap or item_size.numel() != cap or item_qids.numel() != cap * chunk \
+            or item_slot.numel() != cap * chunk:
+        raise ValueError("item array sizes")
+    _check(lib().pw_page_tables(_ptr(bits, torch.int64, "bits"), nq, hkv, n_pages, k_max, chunk,
+                                _ptr(workspace, name="workspace"),
+                                workspace.numel() * workspace.element_size(),
+                                _ptr(item_off, torch.int32, "item_off"),
+                                _ptr(item_kvh, torch.int32, "item_kvh"),
+                                _ptr(item_page, torch.int32, "item_page"),
+                                _ptr(item_qids, torch.int32, "item_qids"),
+                                _ptr(item_size, torch.int32, "item_size"),
+                                _ptr(item_slot, torch.int32, "item_slot"), cap, _stream(stream)))
+
+
+def pw_page_union_prefill(q, k_cache, v_cache, q_pos, kv_len: int, bits, k_max: int, chunk: int,
+                          item_off, item_kvh, item_page, item_qids, item_size, item_slot,
+                          partial_o, partial_lse, out, k_scale=None, v_scale=None,
+                          sm_scale: Optional[float] = None, lse=None, stream=None) -> None:
+    """Attention through page-major items into partials, then their lse merge into out/lse."""
+    nq, hq, d = q.shape
+    hkv, n_pages, page_size, _ = k_cache.shape
+    G = hq // hkv
+    if partial_o.numel() < nq * hkv * k_max * G * d or partial_lse.numel() < nq * hkv * k_max * G:
+        raise ValueError("partial buffers too small")
+    if out.shape != q.shape or out.dtype != torch.bfloat16:
+        raise ValueError("out must be bf16 shaped like q")
+    sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    _check(lib().pw_page_union_prefill(
+        _ptr(q, torch.bfloat16, "q"), nq, hq, hkv, d, _ptr(k_cache, name="k_cache"),
+        _ptr(v_cache, name="v_cache"), _cache_dtype(k_cache), _ptr(k_scale, torch.float32, "k_scale"),
+        _ptr(v_scale, torch.float32, "v_scale"), page_size, n_pages, n_pages * page_size * d,
+        page_size * d, _ptr(q_pos, torch.int32, "q_pos"), kv_len, sm, _ptr(bits, torch.int64, "bits"),
+        k_max, chunk, _ptr(item_off, torch.int32, "item_off"), _ptr(item_kvh, torch.int32, "item_kvh"),
+        _ptr(item_page, torch.int32, "item_page"), _ptr(item_qids, torch.int32, "item_qids"),
+        _ptr(item_size, torch.int32, "item_size"), _ptr(item_slot, torch.int32, "item_slot"),
+        item_kvh.numel(), _ptr(partial_o, torch.bfloat16, "partial_o"),
+        _ptr(partial_lse, torch.float32, "partial_lse"), _ptr(out, torch.bfloat16, "out"),
+        _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
+@dataclass
+class PageUnionPrefill:
+    """The direct KV-page union for TopK supports: page bitsets -> page-major work
+    items (each (KV head, page) once, its selecting queries in chunks) -> attention
+    into per-(query, page) partials -> their lse merge.  Owns the tables and the
+    partial workspace (nq * hq * k * d bf16)."""
+    nq: int
+    hq: int
+    hkv: int
+    d: int
+    n_pages: int
+    page_size: int
+    kv_len: int
+    k: int                      # TopK width: bounds every support size
+    chunk: int = 8              # queries per work item
+    device: str = "cuda"
+
+    def __post_init__(self):
+        dev = self.device
+        i32 = dict(dtype=torch.int32, device=dev)
+        G = self.hq // self.hkv
+        self.bits = torch.empty((self.hkv, self.nq, pw_words(self.n_pages)), dtype=torch.int64, device=dev)
+        self.bad_ids = torch.zeros(1, **i32)
+        ws = pw_page_workspace_bytes(self.nq, self.hkv, self.n_pages)
+        self.workspace = torch.empty(max(-(-ws // 8), 1), dtype=torch.int64, device=dev)
+        cap = max(pw_page_items_capacity(self.nq, self.hkv, self.k, self.n_pages, self.chunk), 1)
+        self.item_off = torch.empty(self.hkv * self.n_pages + 1, **i32)
+        self.item_kvh = torch.empty(cap, **i32)
+        self.item_page = torch.empty(cap, **i32)
+        self.item_size = torch.empty(cap, **i32)
+        self.item_qids = torch.empty((cap, self.chunk), **i32)
+        self.item_slot = torch.empty((cap, self.chunk), **i32)
+        rows = max(self.nq * self.hkv * self.k * G, 1)
+        self.partial_o = torch.empty((rows, self.d), dtype=torch.bfloat16, device=dev)
+        self.partial_lse = torch.empty(rows, dtype=torch.float32, device=dev)
+
+    @property
+    def n_items(self) -> int:
+        return int(self.item_off[-1].item())
+
+    def prepare(self, topk: torch.Tensor, stream=None) -> None:
+        pw_page_bitsets(topk, self.n_pages, self.bits, self.bad_ids, stream)
+        pw_page_tables(self.bits, self.n_pages, self.k, self.chunk, self.workspace, self.item_off,
+                       self.item_kvh, self.item_page, self.item_qids, self.item_size, self.item_slot,
+                       stream)
+
+    def attend(self, q, k_cache, v_cache, q_pos, out, k_scale=None, v_scale=None, lse=None,
+               sm_scale=None, stream=None) -> None:
+        pw_page_union_prefill(q, k_cache, v_cache, q_pos, self.kv_len, self.bits, self.k, self.chunk,
+                              self.item_off, self.item_kvh, self.item_page, self.item_qids,
+                              self.item_size, self.item_slot, self.partial_o, self.partial_lse, out,
+                              k_scale, v_scale, sm_scale, lse, stream)
+
+    def __call__(self, topk, q, k_cache, v_cache, q_pos, out, k_scale=None, v_scale=None, lse=None,
+                 stream=None) -> None:
+        self.prepare(topk, stream)
+        self.attend(q, k_cache, v_cache, q_pos, out, k_scale, v_scale, lse, stream=stream)
 
 
 @dataclass

@@ -12,7 +12,7 @@ BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libpw.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "kvcache.hip", "prep.hip", "attn.hip"]
+SOURCES = ["api.cpp", "kvcache.hip", "prep.hip", "pageunion.hip", "attn.hip"]
 # Packed fp32 ops are disabled for every device compile on this hardware.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -207,6 +207,108 @@ pw_status pw_prepare(const int32_t* topk, int nq, int hkv, int k, int n_pages, i
   return st;
 }
 
+int64_t pw_page_items_capacity(int nq, int hkv, int k_max, int n_pages, int chunk) {
+  if (nq < 0 || hkv < 1 || k_max < 1 || n_pages < 1 || chunk < 1) return -1;
+  const int64_t edges = (int64_t)nq * hkv * std::min(k_max, n_pages);
+  const int64_t n_gp = (int64_t)hkv * n_pages;
+  return std::min(edges, (edges + n_gp * (chunk - 1) + chunk - 1) / chunk);
+}
+
+size_t pw_page_workspace_bytes(int nq, int hkv, int n_pages) {
+  if (nq < 0 || hkv < 1 || n_pages < 1) return 0;
+  return pw::page_workspace_bytes(nq, hkv, n_pages);
+}
+
+pw_status pw_page_tables(const uint64_t* bits, int nq, int hkv, int n_pages, int k_max, int chunk,
+                         void* workspace, size_t workspace_bytes, int32_t* item_off,
+                         int32_t* item_kvh, int32_t* item_page, int32_t* item_qids,
+                         int32_t* item_size, int32_t* item_slot, int64_t item_capacity,
+                         hipStream_t stream) {
+  pw::g_err[0] = 0;
+  if (nq < 0 || hkv < 1 || n_pages < 1 || k_max < 1)
+    return fail(PW_ERR_ARG, "pw_page_tables: bad sizes nq=%d hkv=%d n_pages=%d k_max=%d", nq, hkv,
+                n_pages, k_max);
+  if (chunk < 1 || chunk > 64) return fail(PW_ERR_UNSUPPORTED, "pw_page_tables: chunk=%d not in 1..64", chunk);
+  if (n_pages > 65536) return fail(PW_ERR_UNSUPPORTED, "pw_page_tables: n_pages=%d > 65536", n_pages);
+  if (hkv > 65535 || nq > 64 * 65535)
+    return fail(PW_ERR_UNSUPPORTED, "pw_page_tables: hkv=%d or nq=%d too large", hkv, nq);
+  if ((int64_t)nq * hkv * k_max >= INT32_MAX)
+    return fail(PW_ERR_UNSUPPORTED, "pw_page_tables: nq*hkv*k_max must stay below 2^31");
+  const int64_t need = pw_page_items_capacity(nq, hkv, k_max, n_pages, chunk);
+  if (item_capacity < need)
+    return fail(PW_ERR_CAPACITY, "pw_page_tables: item_capacity %lld < %lld", (long long)item_capacity,
+                (long long)need);
+  if (workspace_bytes < pw::page_workspace_bytes(nq, hkv, n_pages))
+    return fail(PW_ERR_CAPACITY, "pw_page_tables: workspace_bytes %zu < %zu", workspace_bytes,
+                pw::page_workspace_bytes(nq, hkv, n_pages));
+  if (!item_off) return fail(PW_ERR_ARG, "pw_page_tables: null item_off");
+  if (nq > 0 && (!bits || !workspace || !item_kvh || !item_page || !item_qids || !item_size || !item_slot))
+    return fail(PW_ERR_ARG, "pw_page_tables: null required pointer");
+  if ((uintptr_t)workspace % 8) return fail(PW_ERR_ARG, "pw_page_tables: workspace must be 8-byte aligned");
+  return pw::launch_page_tables(bits, nq, hkv, n_pages, k_max, chunk, workspace, item_off, item_kvh,
+                                item_page, item_qids, item_size, item_slot, item_capacity, stream);
+}
+
+pw_status pw_page_union_prefill(const void* q, int nq, int hq, int hkv, int d, const void* k_cache,
+                                const void* v_cache, int kv_dtype, const float* k_scale,
+                                const float* v_scale, int page_size, int n_pages,
+                                int64_t stride_head, int64_t stride_page, const int32_t* q_pos,
+                                int kv_len, float sm_scale, const uint64_t* bits, int k_max,
+                                int chunk, const int32_t* item_off, const int32_t* item_kvh,
+                                const int32_t* item_page, const int32_t* item_qids,
+                                const int32_t* item_size, const int32_t* item_slot,
+                                int64_t item_capacity, void* partial_o, float* partial_lse,
+                                void* out, float* lse, hipStream_t stream) {
+  pw::g_err[0] = 0;
+  if (nq < 0 || hq < 1 || hkv < 1 || n_pages < 1 || kv_len < 0 || k_max < 1 || item_capacity < 0)
+    return fail(PW_ERR_ARG, "pw_page_union_prefill: bad sizes nq=%d hq=%d hkv=%d n_pages=%d k_max=%d",
+                nq, hq, hkv, n_pages, k_max);
+  if (hq % hkv) return fail(PW_ERR_ARG, "pw_page_union_prefill: hq=%d not a multiple of hkv=%d", hq, hkv);
+  const int G = hq / hkv;
+  if (d != 64 && d != 128) return fail(PW_ERR_UNSUPPORTED, "pw_page_union_prefill: d=%d (64 or 128)", d);
+  if (page_size != 64 && page_size != 128)
+    return fail(PW_ERR_UNSUPPORTED, "pw_page_union_prefill: page_size=%d (64 or 128)", page_size);
+  if (kv_dtype != PW_KV_BF16 && kv_dtype != PW_KV_FP8_E4M3)
+    return fail(PW_ERR_UNSUPPORTED, "pw_page_union_prefill: kv_dtype=%d", kv_dtype);
+  if (chunk < 1 || chunk > 64 || (int64_t)G * chunk > pw::max_rows_per_item(d, kv_dtype))
+    return fail(PW_ERR_UNSUPPORTED, "pw_page_union_prefill: chunk=%d (1..64, (hq/hkv)*chunk <= %d)",
+                chunk, pw::max_rows_per_item(d, kv_dtype));
+  if ((int64_t)k_max * G > 16384)
+    return fail(PW_ERR_UNSUPPORTED, "pw_page_union_prefill: k_max*(hq/hkv)=%lld > 16384",
+                (long long)k_max * G);
+  if ((int64_t)nq * hkv * k_max >= INT32_MAX)
+    return fail(PW_ERR_UNSUPPORTED, "pw_page_union_prefill: nq*hkv*k_max must stay below 2^31");
+  if (item_capacity >= INT32_MAX / 8)
+    return fail(PW_ERR_UNSUPPORTED, "pw_page_union_prefill: item_capacity too large");
+  const int esz = kv_dtype == PW_KV_FP8_E4M3 ? 1 : 2;
+  if (stride_page < (int64_t)page_size * d || stride_head < 0)
+    return fail(PW_ERR_ARG, "pw_page_union_prefill: stride_page < page_size*d or stride_head < 0");
+  if ((stride_page * esz) % 16 || (stride_head * esz) % 16)
+    return fail(PW_ERR_ARG, "pw_page_union_prefill: strides must be multiples of 16 bytes");
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out | (uintptr_t)partial_o) % 16)
+    return fail(PW_ERR_ARG, "pw_page_union_prefill: q, caches, partial_o and out must be 16-byte aligned");
+  if (!(sm_scale > 0.f)) return fail(PW_ERR_ARG, "pw_page_union_prefill: sm_scale must be positive");
+  if (nq == 0) return PW_OK;
+  if (!q || !k_cache || !v_cache || !q_pos || !bits || !item_off || !item_kvh || !item_page ||
+      !item_qids || !item_size || !item_slot || !partial_o || !partial_lse || !out)
+    return fail(PW_ERR_ARG, "pw_page_union_prefill: null required pointer");
+  if (kv_dtype == PW_KV_FP8_E4M3 && (!k_scale || !v_scale))
+    return fail(PW_ERR_ARG, "pw_page_union_prefill: fp8 KV needs k_scale and v_scale");
+  if (item_capacity > 0) {
+    pw::AttnArgs a{q, nq, hq, hkv, d, k_cache, v_cache, kv_dtype, k_scale, v_scale, page_size,
+                   n_pages, stride_head, stride_page, q_pos, kv_len, sm_scale, item_qids,
+                   item_size, (int)item_capacity, chunk, 0, nullptr, item_page, nullptr,
+                   item_capacity, partial_o, partial_lse};
+    a.item_kvh = item_kvh;
+    a.n_items_dev = item_off + (int64_t)hkv * n_pages;
+    a.out_slot = item_slot;
+    const pw_status st = pw::launch_sparse_prefill(a, stream);
+    if (st != PW_OK) return st;
+  }
+  return pw::launch_page_merge(bits, nq, hkv, G, d, n_pages, k_max, partial_o, partial_lse, out,
+                               lse, stream);
+}
+
 pw_status pw_sparse_prefill(const void* q, int nq, int hq, int hkv, int d, const void* k_cache,
                             const void* v_cache, int kv_dtype, const float* k_scale,
                             const float* v_scale, int page_size, int n_pages, int64_t stride_head,

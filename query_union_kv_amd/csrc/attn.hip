@@ -75,6 +75,9 @@ struct Params {
   const uint8_t* union_qmask;
   uint16_t* out;
   float* lse;
+  const int32_t* item_kvh;      // page-major items (else NULL): KV head of each item
+  const int32_t* n_items_dev;   // page-major items: device item count (n_items bounds it)
+  const int32_t* out_slot;      // page-major items: partial slot per (item, member)
   int64_t stride_head_b;   // bytes
   int64_t stride_page_b;   // bytes
   int64_t capacity;
@@ -164,9 +167,15 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   // range of items (KV-head-major), so one XCD's L2 serves neighbouring groups of the
   // same KV head.
   const int b = blockIdx.x;
-  const int item = (b & 7) * p.items_per_xcd + (b >> 3);
-  if (item >= p.n_items) return;
-  const int g = item / p.n_groups;
+  int n_items = p.n_items, per_xcd = p.items_per_xcd;
+  if (p.n_items_dev) {   // page-major: the grid is an upper bound of the device count
+    n_items = min(n_items, *p.n_items_dev);
+    per_xcd = (n_items + 7) >> 3;
+    if ((b >> 3) >= per_xcd) return;
+  }
+  const int item = (b & 7) * per_xcd + (b >> 3);
+  if (item >= n_items) return;
+  const int g = p.item_kvh ? p.item_kvh[item] : item / p.n_groups;
   const int j = item - g * p.n_groups;
 
   const int tid = threadIdx.x;
@@ -184,7 +193,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   } else {
     gsize = min(p.max_group, p.nq - j * p.max_group);
   }
-  int qid[MT], hh[MT], row_lim[MT], my_bit[MT], mt_members[MT], mt_lim[MT];
+  int qid[MT], hh[MT], row_lim[MT], my_bit[MT], mt_members[MT], mt_lim[MT], slot[MT];
   bf16x8 qf[MT][C::kDc];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
@@ -195,6 +204,11 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     int id = -1;
     if (member < gsize) id = qids ? qids[member] : j * p.max_group + member;
     if (id >= p.nq) id = -1;
+    slot[m] = -1;
+    if (p.out_slot && id >= 0) {
+      slot[m] = p.out_slot[(int64_t)item * p.max_group + member];
+      if (slot[m] < 0) id = -1;
+    }
     qid[m] = id;
     const int qpos = id >= 0 ? p.q_pos[id] : -1;
     row_lim[m] = min(qpos, p.kv_len - 1);          // last usable token of this row
@@ -229,8 +243,13 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 
   // ---- table of this item -----------------------------------------------------------
   const int table = p.shared_table ? g : item;
-  const int64_t e_begin = min<int64_t>(max(p.union_off[table], 0), p.capacity);
-  const int64_t e_end = min<int64_t>(p.union_off[table + 1], p.capacity);
+  int64_t e_begin = item, e_end = item + 1;   // page-major items: one page each
+  if (p.union_off) {
+    e_begin = p.union_off[table];
+    e_end = p.union_off[table + 1];
+  }
+  e_begin = min<int64_t>(max<int64_t>(e_begin, 0), p.capacity);
+  e_end = min<int64_t>(e_end, p.capacity);
   const int tpp_shift = p.page_size == 128 ? 2 : 1;          // log2(tiles per page)
   const int n_tiles = (int)max<int64_t>(e_end - e_begin, 0) << tpp_shift;
 
@@ -488,7 +507,9 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   for (int m = 0; m < MT; ++m) {
     if (qid[m] < 0) continue;
     const float inv = l_run[m] > 0.f ? 1.0f / l_run[m] : 0.f;
-    uint16_t* dst = p.out + ((int64_t)qid[m] * p.hq + hh[m]) * D;
+    const int64_t orow = p.out_slot ? (int64_t)slot[m] * p.G + (hh[m] - g * p.G)
+                                    : (int64_t)qid[m] * p.hq + hh[m];
+    uint16_t* dst = p.out + orow * D;
 #pragma unroll
     for (int dt = 0; dt < C::kDt; ++dt) {
       const bf16x4 v{(__bf16)(o[m][dt][0] * inv), (__bf16)(o[m][dt][1] * inv),
@@ -496,8 +517,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
       *reinterpret_cast<bf16x4*>(dst + 16 * dt + 4 * lq) = v;
     }
     if (p.lse && lq == 0)
-      p.lse[(int64_t)qid[m] * p.hq + hh[m]] =
-          l_run[m] > 0.f ? (m_ref[m] + __log2f(l_run[m])) * kLn2 : -INFINITY;
+      p.lse[orow] = l_run[m] > 0.f ? (m_ref[m] + __log2f(l_run[m])) * kLn2 : -INFINITY;
   }
 }
 
@@ -563,6 +583,9 @@ pw_status launch_sparse_prefill(const AttnArgs& a, hipStream_t stream) {
   p.union_qmask = a.union_qmask;
   p.out = static_cast<uint16_t*>(a.out);
   p.lse = a.lse;
+  p.item_kvh = a.item_kvh;
+  p.n_items_dev = a.n_items_dev;
+  p.out_slot = a.out_slot;
   const int esz = a.kv_dtype == PW_KV_FP8_E4M3 ? 1 : 2;
   p.stride_head_b = a.stride_head * esz;
   p.stride_page_b = a.stride_page * esz;
@@ -577,7 +600,7 @@ pw_status launch_sparse_prefill(const AttnArgs& a, hipStream_t stream) {
   p.n_groups = a.n_groups;
   p.max_group = a.max_group;
   p.shared_table = a.shared_table;
-  p.n_items = a.hkv * a.n_groups;
+  p.n_items = a.item_kvh ? a.n_groups : a.hkv * a.n_groups;   // page-major: capacity
   p.items_per_xcd = (p.n_items + 7) / 8;
   p.score_scale = a.sm_scale * kLog2e;
   if (p.n_items == 0) return PW_OK;

@@ -41,6 +41,20 @@ pw_status launch_prepare(const int32_t* topk, int nq, int hkv, int k, int n_page
                          int32_t* union_pages, uint8_t* union_qmask, int64_t capacity,
                          hipStream_t stream);
 
+// Exclusive prefix sum in place: off[1..n] hold counts; afterwards off[i] = sum of the
+// first i counts (off[0] = 0).  One workgroup.
+pw_status launch_scan(int32_t* off, int n, hipStream_t stream);
+
+// Page-major work items of the direct KV-page union, and the lse merge of its partials.
+size_t page_workspace_bytes(int nq, int hkv, int n_pages);
+pw_status launch_page_tables(const uint64_t* bits, int nq, int hkv, int n_pages, int k_max,
+                             int chunk, void* workspace, int32_t* item_off, int32_t* item_kvh,
+                             int32_t* item_page, int32_t* item_qids, int32_t* item_size,
+                             int32_t* item_slot, int64_t item_capacity, hipStream_t stream);
+pw_status launch_page_merge(const uint64_t* bits, int nq, int hkv, int G, int d, int n_pages,
+                            int k_max, const void* part_o, const float* part_lse, void* out,
+                            float* lse, hipStream_t stream);
+
 struct AttnArgs {
   const void* q;
   int nq, hq, hkv, d;
@@ -63,6 +77,12 @@ struct AttnArgs {
   int64_t capacity;
   void* out;
   float* lse;
+  // Page-major items (all NULL otherwise): item i runs for KV head item_kvh[i] over the
+  // one page union_pages[i]; the item count is read from n_items_dev (n_groups bounds it);
+  // member j's row goes to partial row out_slot[i * max_group + j] * G + (h - g*G).
+  const int32_t* item_kvh = nullptr;
+  const int32_t* n_items_dev = nullptr;
+  const int32_t* out_slot = nullptr;
 };
 
 pw_status launch_sparse_prefill(const AttnArgs& a, hipStream_t stream);

@@ -528,6 +528,11 @@ __global__ void k_union_emit(const uint64_t* __restrict__ bits, int n_rows, int 
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
+pw_status launch_scan(int32_t* off, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(k_union_scan, dim3(1), dim3(1024), 0, stream, off, n);
+  return check_launch("prefix sum");
+}
+
 pw_status launch_page_bitsets(const int32_t* topk, int n_rows, int hkv, int k, int n_pages,
                               uint64_t* bits, int32_t* bad_id_count, hipStream_t stream) {
   const int words = (n_pages + 63) / 64;

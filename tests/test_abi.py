@@ -166,3 +166,54 @@ def test_append_validation(kw, code):
 
 def test_append_nothing_to_do_is_ok():
     assert _append(n_tok=0)[0] == 0
+
+
+def test_page_workspace_bytes():
+    assert pw.pw_page_workspace_bytes(4096, 8, 1024) == 8 * 1024 * 64 * 8 + 8 * 4096 * 16 * 4
+    assert pw.pw_page_workspace_bytes(0, 1, 1) == 0 and pw.pw_page_workspace_bytes(-1, 1, 1) == 0
+
+
+def test_page_items_capacity():
+    assert pw.pw_page_items_capacity(4096, 8, 16, 1024, 8) == (4096 * 8 * 16 + 8192 * 7 + 7) // 8
+    assert pw.pw_page_items_capacity(10, 1, 4, 2, 8) == (10 * 2 + 2 * 7 + 7) // 8   # k_max capped at n_pages
+    assert pw.pw_page_items_capacity(3, 1, 4, 100, 8) == 12                          # items <= edges
+    assert pw.pw_page_items_capacity(-1, 1, 4, 2, 8) == -1
+
+
+@pytest.mark.parametrize("args,code", [
+    # bits, nq, hkv, n_pages, k_max, chunk, ws, ws_bytes, off, kvh, page, qids, size, slot, cap, stream
+    ((NULL, 64, 1, 16, 4, 0, NULL, 1 << 20, NULL, NULL, NULL, NULL, NULL, NULL, 1000, NULL), -2),  # chunk 0
+    ((NULL, 64, 1, 16, 4, 65, NULL, 1 << 20, NULL, NULL, NULL, NULL, NULL, NULL, 1000, NULL), -2), # chunk 65
+    ((NULL, 64, 1, 70000, 4, 8, NULL, 1 << 30, NULL, NULL, NULL, NULL, NULL, NULL, 10 ** 6, NULL), -2),
+    ((NULL, 64, 1, 16, 0, 8, NULL, 1 << 20, NULL, NULL, NULL, NULL, NULL, NULL, 1000, NULL), -1),  # k_max 0
+    ((NULL, 64, 1, 16, 4, 8, NULL, 1 << 20, NULL, NULL, NULL, NULL, NULL, NULL, 33, NULL), -3),    # capacity
+    ((NULL, 64, 1, 16, 4, 8, NULL, 100, NULL, NULL, NULL, NULL, NULL, NULL, 1000, NULL), -3),      # workspace
+    ((NULL, 64, 1, 16, 4, 8, NULL, 1 << 20, NULL, NULL, NULL, NULL, NULL, NULL, 1000, NULL), -1),  # nulls
+])
+def test_page_tables_validation(args, code):
+    st, msg = _err(L.pw_page_tables(*args))
+    assert st == code and msg.startswith("pw_page_tables"), msg
+
+
+def _page_attn(**kw):
+    a = dict(q=NULL, nq=8, hq=4, hkv=1, d=128, k=NULL, v=NULL, kv_dtype=0, ks=NULL, vs=NULL, ps=64,
+             n_pages=4, sh=4 * 64 * 128, sp=64 * 128, q_pos=NULL, kv_len=256, sm=0.088, bits=NULL,
+             k_max=4, chunk=8, off=NULL, kvh=NULL, page=NULL, qids=NULL, size=NULL, slot=NULL,
+             cap=16, po=NULL, pl=NULL, out=NULL, lse=NULL, stream=NULL)
+    a.update(kw)
+    return _err(L.pw_page_union_prefill(*a.values()))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), -2), (dict(ps=32), -2), (dict(hq=6, hkv=4), -1), (dict(kv_dtype=2), -2),
+    (dict(chunk=65), -2), (dict(chunk=0), -2), (dict(hq=64, chunk=8), -2),  # 64 * 8 rows > 256
+    (dict(k_max=0), -1), (dict(k_max=5000), -2),                           # k_max * G > 16384
+    (dict(sp=100), -1), (dict(sm=0.0), -1), (dict(), -1),
+])
+def test_page_union_validation(kw, code):
+    st, msg = _page_attn(**kw)
+    assert st == code and msg.startswith("pw_page_union_prefill"), msg
+
+
+def test_page_union_nothing_to_do_is_ok():
+    assert _page_attn(nq=0)[0] == 0
