@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=None,
                     help="run only this many steps after warmup (for rocprofv3), no extras")
+    ap.add_argument("--profile-path", choices=["union", "page"], default="union",
+                    help="with --profile-steps: the query-union call (default) or the direct KV-page union")
     ap.add_argument("--calibrate-copy", type=int, default=None, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (counter calibration)")
     return ap.parse_args()
@@ -174,16 +176,22 @@ def main():
         if evs:
             evs[2].record(stream)
 
+    if args.profile_steps is not None:
+        run = step
+        if args.profile_path == "page":
+            pu = pw.PageUnionPrefill(nq=cfg.nq, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, n_pages=cfg.n_pages,
+                                     page_size=cfg.ps, kv_len=cfg.kv_len, k=ids.shape[2], device=dev)
+            run = lambda: pu(ids, q, kc, vc, q_pos, out, ks, vs, stream=stream)   # noqa: E731
+        for _ in range(args.warmup + args.profile_steps):
+            run()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps, "warmup": args.warmup, "workload": cfg.name,
+                          "path": args.profile_path}))
+        return
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
-    if args.profile_steps is not None:
-        for _ in range(args.profile_steps):
-            step()
-        torch.cuda.synchronize()
-        print(json.dumps({"profile_steps": args.profile_steps, "workload": cfg.name}))
-        return
 
     # ---- the timed region: K complete steps back to back -------------------------------
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -269,7 +277,7 @@ def main():
         partial_bytes = 2 * selected * cfg.g * (cfg.d * 2 + 4)          # written, then read by the merge
         extras["direct_page_union"] = {
             "call_ms": t_pu_call, "prep_ms": t_pu_prep, "attn_and_merge_ms": t_pu_attn,
-            "queries_per_s": cfg.nq / (t_pu_call / 1e3), "items": n_items,
+            "queries_per_s": cfg.nq / (t_pu_call / 1e3), "items": n_items, "chunk": pu.chunk,
             "distinct_kv_bytes": distinct * page_bytes, "partial_bytes": partial_bytes,
             "max_abs_vs_union": float((out_pu.float() - out.float()).abs().max().item())}
         del pu, out_pu

@@ -346,13 +346,15 @@ class PageUnionPrefill:
     page_size: int
     kv_len: int
     k: int                      # TopK width: bounds every support size
-    chunk: int = 8              # queries per work item
+    chunk: int = 0              # queries per work item (0: 64 query-head rows per item)
     device: str = "cuda"
 
     def __post_init__(self):
         dev = self.device
         i32 = dict(dtype=torch.int32, device=dev)
         G = self.hq // self.hkv
+        if self.chunk <= 0:
+            self.chunk = max(1, min(64, 64 // G))
         self.bits = torch.empty((self.hkv, self.nq, pw_words(self.n_pages)), dtype=torch.int64, device=dev)
         self.bad_ids = torch.zeros(1, **i32)
         ws = pw_page_workspace_bytes(self.nq, self.hkv, self.n_pages)

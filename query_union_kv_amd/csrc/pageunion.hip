@@ -226,12 +226,21 @@ __global__ __launch_bounds__(64) void k_page_merge(
   for (int c = lane; c < G * kC; c += kWave) {
     const int hl = c / kC, e0 = (c - hl * kC) * 8;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < n; ++r) {
-      const float w = wts[r * G + hl];
-      if (w == 0.f) continue;
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(part_o + ((slot0 + r) * G + hl) * D + e0);
+    const uint16_t* src = part_o + (slot0 * G + hl) * D + e0;
+    // every partial row below n was written (a page without usable keys has o = 0 and
+    // weight 0), so the loads need no guard; batches of 8 keep them all in flight
+    for (int r0 = 0; r0 < n; r0 += 8) {
+      bf16x8 v[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] += w * (float)v[k];
+      for (int i = 0; i < 8; ++i)
+        if (r0 + i < n) v[i] = *reinterpret_cast<const bf16x8*>(src + (int64_t)(r0 + i) * G * D);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (r0 + i >= n) break;
+        const float w = wts[(r0 + i) * G + hl];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] += w * (float)v[i][k];
+      }
     }
     bf16x8 o;
 #pragma unroll
