@@ -3,6 +3,7 @@
 // in include/pw.h.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <algorithm>
 
@@ -294,19 +295,37 @@ pw_status pw_page_union_prefill(const void* q, int nq, int hq, int hkv, int d, c
     return fail(PW_ERR_ARG, "pw_page_union_prefill: null required pointer");
   if (kv_dtype == PW_KV_FP8_E4M3 && (!k_scale || !v_scale))
     return fail(PW_ERR_ARG, "pw_page_union_prefill: fp8 KV needs k_scale and v_scale");
-  if (item_capacity > 0) {
-    pw::AttnArgs a{q, nq, hq, hkv, d, k_cache, v_cache, kv_dtype, k_scale, v_scale, page_size,
-                   n_pages, stride_head, stride_page, q_pos, kv_len, sm_scale, item_qids,
-                   item_size, (int)item_capacity, chunk, 0, nullptr, item_page, nullptr,
-                   item_capacity, partial_o, partial_lse};
-    a.item_kvh = item_kvh;
-    a.n_items_dev = item_off + (int64_t)hkv * n_pages;
-    a.out_slot = item_slot;
-    const pw_status st = pw::launch_sparse_prefill(a, stream);
+  // KV heads run in batches of a few heads, so that a batch's partial rows (written by the
+  // attention, read back by the merge) are mostly still in the 256 MB last-level cache.
+  // When one head's partials alone exceed that, batching gains nothing: all heads at once.
+  const int64_t part_per_head = (int64_t)nq * k_max * G * (d * 2 + 4);
+  int hb = (int)std::min<int64_t>(hkv, (320ll << 20) / std::max<int64_t>(part_per_head, 1));
+  if (hb < 2) hb = hkv;
+  if (const char* e = getenv("PW_PAGE_HEAD_BATCH")) {
+    const int v = atoi(e);
+    if (v >= 1) hb = std::min(v, hkv);
+  }
+  for (int g0 = 0; g0 < hkv; g0 += hb) {
+    const int g1 = std::min(hkv, g0 + hb);
+    const int64_t cap = std::min<int64_t>(item_capacity,
+                                          pw_page_items_capacity(nq, g1 - g0, k_max, n_pages, chunk));
+    if (cap > 0) {
+      pw::AttnArgs a{q, nq, hq, hkv, d, k_cache, v_cache, kv_dtype, k_scale, v_scale, page_size,
+                     n_pages, stride_head, stride_page, q_pos, kv_len, sm_scale, item_qids,
+                     item_size, (int)cap, chunk, 0, nullptr, item_page, nullptr,
+                     item_capacity, partial_o, partial_lse};
+      a.item_kvh = item_kvh;
+      a.item_lo_dev = item_off + (int64_t)g0 * n_pages;
+      a.item_hi_dev = item_off + (int64_t)g1 * n_pages;
+      a.out_slot = item_slot;
+      const pw_status st = pw::launch_sparse_prefill(a, stream);
+      if (st != PW_OK) return st;
+    }
+    const pw_status st = pw::launch_page_merge(bits, nq, hkv, g0, g1, G, d, n_pages, k_max,
+                                               partial_o, partial_lse, out, lse, stream);
     if (st != PW_OK) return st;
   }
-  return pw::launch_page_merge(bits, nq, hkv, G, d, n_pages, k_max, partial_o, partial_lse, out,
-                               lse, stream);
+  return PW_OK;
 }
 
 pw_status pw_sparse_prefill(const void* q, int nq, int hq, int hkv, int d, const void* k_cache,

@@ -76,7 +76,8 @@ struct Params {
   uint16_t* out;
   float* lse;
   const int32_t* item_kvh;      // page-major items (else NULL): KV head of each item
-  const int32_t* n_items_dev;   // page-major items: device item count (n_items bounds it)
+  const int32_t* item_lo_dev;   // page-major items: run items [*item_lo_dev, *item_hi_dev)
+  const int32_t* item_hi_dev;   //   (n_items bounds their count)
   const int32_t* out_slot;      // page-major items: partial slot per (item, member)
   int64_t stride_head_b;   // bytes
   int64_t stride_page_b;   // bytes
@@ -167,14 +168,16 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   // range of items (KV-head-major), so one XCD's L2 serves neighbouring groups of the
   // same KV head.
   const int b = blockIdx.x;
-  int n_items = p.n_items, per_xcd = p.items_per_xcd;
-  if (p.n_items_dev) {   // page-major: the grid is an upper bound of the device count
-    n_items = min(n_items, *p.n_items_dev);
+  int n_items = p.n_items, per_xcd = p.items_per_xcd, item0 = 0;
+  if (p.item_lo_dev) {   // page-major: the grid is an upper bound of the device count
+    item0 = *p.item_lo_dev;
+    n_items = min(n_items, *p.item_hi_dev - item0);
     per_xcd = (n_items + 7) >> 3;
     if ((b >> 3) >= per_xcd) return;
   }
-  const int item = (b & 7) * per_xcd + (b >> 3);
-  if (item >= n_items) return;
+  const int item_rel = (b & 7) * per_xcd + (b >> 3);
+  if (item_rel >= n_items) return;
+  const int item = item0 + item_rel;
   const int g = p.item_kvh ? p.item_kvh[item] : item / p.n_groups;
   const int j = item - g * p.n_groups;
 
@@ -584,7 +587,8 @@ pw_status launch_sparse_prefill(const AttnArgs& a, hipStream_t stream) {
   p.out = static_cast<uint16_t*>(a.out);
   p.lse = a.lse;
   p.item_kvh = a.item_kvh;
-  p.n_items_dev = a.n_items_dev;
+  p.item_lo_dev = a.item_lo_dev;
+  p.item_hi_dev = a.item_hi_dev;
   p.out_slot = a.out_slot;
   const int esz = a.kv_dtype == PW_KV_FP8_E4M3 ? 1 : 2;
   p.stride_head_b = a.stride_head * esz;

@@ -51,9 +51,9 @@ pw_status launch_page_tables(const uint64_t* bits, int nq, int hkv, int n_pages,
                              int chunk, void* workspace, int32_t* item_off, int32_t* item_kvh,
                              int32_t* item_page, int32_t* item_qids, int32_t* item_size,
                              int32_t* item_slot, int64_t item_capacity, hipStream_t stream);
-pw_status launch_page_merge(const uint64_t* bits, int nq, int hkv, int G, int d, int n_pages,
-                            int k_max, const void* part_o, const float* part_lse, void* out,
-                            float* lse, hipStream_t stream);
+pw_status launch_page_merge(const uint64_t* bits, int nq, int hkv, int g0, int g1, int G, int d,
+                            int n_pages, int k_max, const void* part_o, const float* part_lse,
+                            void* out, float* lse, hipStream_t stream);
 
 struct AttnArgs {
   const void* q;
@@ -78,10 +78,12 @@ struct AttnArgs {
   void* out;
   float* lse;
   // Page-major items (all NULL otherwise): item i runs for KV head item_kvh[i] over the
-  // one page union_pages[i]; the item count is read from n_items_dev (n_groups bounds it);
-  // member j's row goes to partial row out_slot[i * max_group + j] * G + (h - g*G).
+  // one page union_pages[i]; the items [*item_lo_dev, *item_hi_dev) run (n_groups bounds
+  // their count); member j's row goes to partial row out_slot[i * max_group + j] * G +
+  // (h - g*G).
   const int32_t* item_kvh = nullptr;
-  const int32_t* n_items_dev = nullptr;
+  const int32_t* item_lo_dev = nullptr;
+  const int32_t* item_hi_dev = nullptr;
   const int32_t* out_slot = nullptr;
 };
 

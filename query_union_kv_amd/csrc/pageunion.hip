@@ -189,13 +189,13 @@ __global__ void k_fill_i32(int32_t* __restrict__ p, int n, int v) {
 // Dynamic LDS: k_max * G floats per wave (the weights).
 template <int D>
 __global__ __launch_bounds__(64) void k_page_merge(
-    const uint64_t* __restrict__ bits, int nq, int hkv, int G, int words, int k_max,
+    const uint64_t* __restrict__ bits, int nq, int hkv, int g0, int hb, int G, int words, int k_max,
     const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
   extern __shared__ float wts[];
   const int lane = threadIdx.x;
-  const int qg = blockIdx.x;
-  const int q = qg / hkv, g = qg - q * hkv;
+  const int qg = blockIdx.x;                   // KV heads g0 .. g0 + hb - 1
+  const int q = qg / hb, g = g0 + (qg - q * hb);
   if (q >= nq) return;
   const uint64_t* row = bits + ((int64_t)g * nq + q) * words;
   int n = 0;
@@ -285,18 +285,19 @@ pw_status launch_page_tables(const uint64_t* bits, int nq, int hkv, int n_pages,
   return check_launch("pw_page_tables");
 }
 
-pw_status launch_page_merge(const uint64_t* bits, int nq, int hkv, int G, int d, int n_pages,
-                            int k_max, const void* part_o, const float* part_lse, void* out,
-                            float* lse, hipStream_t stream) {
+pw_status launch_page_merge(const uint64_t* bits, int nq, int hkv, int g0, int g1, int G, int d,
+                            int n_pages, int k_max, const void* part_o, const float* part_lse,
+                            void* out, float* lse, hipStream_t stream) {
   const int words = (n_pages + 63) / 64;
   const size_t lds = (size_t)k_max * G * sizeof(float);
-  const dim3 grid((unsigned)((int64_t)nq * hkv));
+  const int hb = g1 - g0;
+  const dim3 grid((unsigned)((int64_t)nq * hb));
   if (d == 128)
-    hipLaunchKernelGGL(k_page_merge<128>, grid, dim3(64), lds, stream, bits, nq, hkv, G, words,
-                       k_max, (const uint16_t*)part_o, part_lse, (uint16_t*)out, lse);
+    hipLaunchKernelGGL(k_page_merge<128>, grid, dim3(64), lds, stream, bits, nq, hkv, g0, hb, G,
+                       words, k_max, (const uint16_t*)part_o, part_lse, (uint16_t*)out, lse);
   else
-    hipLaunchKernelGGL(k_page_merge<64>, grid, dim3(64), lds, stream, bits, nq, hkv, G, words,
-                       k_max, (const uint16_t*)part_o, part_lse, (uint16_t*)out, lse);
+    hipLaunchKernelGGL(k_page_merge<64>, grid, dim3(64), lds, stream, bits, nq, hkv, g0, hb, G,
+                       words, k_max, (const uint16_t*)part_o, part_lse, (uint16_t*)out, lse);
   return check_launch("pw_page_union_prefill (merge)");
 }
 

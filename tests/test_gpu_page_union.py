@@ -146,3 +146,15 @@ def test_repeated_calls_are_identical():
     a = run_page(w)
     b = run_page(w)
     assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["lse"], b["lse"])
+
+
+def test_kv_head_batches_give_identical_results(monkeypatch):
+    """Running the KV heads in batches (attention then merge per batch) changes only the
+    order of launches, so every bit of the output is the same."""
+    w = make_workload(_small(nq=150, k=8, kv_len=2048, hq=16, hkv=4, kv_dtype="fp8"))
+    monkeypatch.delenv("PW_PAGE_HEAD_BATCH", raising=False)
+    a = run_page(w, chunk=8)
+    for hb in ("1", "3"):
+        monkeypatch.setenv("PW_PAGE_HEAD_BATCH", hb)
+        b = run_page(w, chunk=8)
+        assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["lse"], b["lse"]), hb
