@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--cpu-queries", type=int, default=4096,
                     help="oracle sample: the first N queries (whole windows), all KV heads")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-chunked", action="store_true",
+                    help="skip the chunked-prefill leg (whole context in chunks of nq, overlap vs serial)")
     ap.add_argument("--profile-steps", type=int, default=None,
                     help="run only this many steps after warmup (for rocprofv3), no extras")
     ap.add_argument("--profile-path", choices=["union", "page"], default="union",
@@ -304,6 +306,45 @@ def main():
     extras["append_kv"] = {"ms": t_app, "bytes": app_bytes, "GBs": app_bytes / (t_app / 1e3) / 1e9,
                            "hbm_frac": app_bytes / (t_app / 1e3) / 1e9 / HBM_PEAK_GBS}
     del kc2, vc2, ks2, vs2
+
+    # ---- chunked prefill of the whole context: append -> prepare -> attend per chunk, the
+    # next chunk's preparation overlapped on a second stream vs all on one stream ----------
+    if mode == "topk" and not args.no_chunked and cfg.kv_len % cfg.nq == 0:
+        from workloads import make_supports
+        n_chunks = cfg.kv_len // cfg.nq
+        runner = pw.ChunkedPrefill(hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, n_pages=cfg.n_pages, page_size=cfg.ps,
+                                   max_chunk=cfg.nq, k=cfg.k, window=cfg.window, max_group=cfg.max_group,
+                                   device=dev)
+        kc3, vc3 = kc.clone(), vc.clone()
+        ks3, vs3 = (ks.clone(), vs.clone()) if ks is not None else (None, None)
+        chunk_list = []
+        for c in range(n_chunks):
+            ccfg = cfg.scaled(kv_len=cfg.nq * (c + 1))
+            qp, tk, _ = make_supports(ccfg, seed=cfg.seed * 1000 + c)
+            chunk_list.append(dict(q=q, k_new=kn, v_new=vn, topk=torch.from_numpy(np.ascontiguousarray(tk)).to(dev),
+                                   q_pos=torch.from_numpy(qp).to(dev), first_token=cfg.nq * c,
+                                   out=torch.empty_like(q)))
+
+        def chunked(overlap):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            runner.run(chunk_list, kc3, vc3, ks3, vs3, overlap=overlap, stream=stream)   # warm
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(3):
+                e0.record(stream)
+                runner.run(chunk_list, kc3, vc3, ks3, vs3, overlap=overlap, stream=stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            return statistics.median(ts)
+
+        t_ser = chunked(False)
+        t_ovl = chunked(True)
+        extras["chunked_prefill"] = {
+            "chunks": n_chunks, "chunk_queries": cfg.nq, "context": cfg.kv_len,
+            "serial_ms": t_ser, "overlapped_ms": t_ovl, "saving_ms": t_ser - t_ovl,
+            "queries_per_s_overlapped": cfg.kv_len / (t_ovl / 1e3)}
+        del kc3, vc3, ks3, vs3, chunk_list, runner
 
     # ---- flushed timing: 512 MiB written before each step, outside the event pair ----------
     if args.flush_steps:

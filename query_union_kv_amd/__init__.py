@@ -474,8 +474,9 @@ class SparsePrefill:
                             self.union_off, self.union_pages, None, stream)
 
     def attend(self, q, k_cache, v_cache, q_pos, out, k_scale=None, v_scale=None, lse=None,
-               sm_scale=None, stream=None) -> None:
-        pw_sparse_prefill(q, k_cache, v_cache, q_pos, self.kv_len, self.union_off, self.union_pages,
+               sm_scale=None, stream=None, kv_len: Optional[int] = None) -> None:
+        kv_len = self.kv_len if kv_len is None else kv_len
+        pw_sparse_prefill(q, k_cache, v_cache, q_pos, kv_len, self.union_off, self.union_pages,
                           out, hkv=self.hkv, n_groups=self.n_groups, max_group=self.max_group,
                           group_qids=self.group_qids, group_size=self.group_size,
                           union_qmask=self.union_qmask, k_scale=k_scale, v_scale=v_scale,
@@ -486,3 +487,75 @@ class SparsePrefill:
                  stream=None) -> None:
         self.prepare(ids, stream)
         self.attend(q, k_cache, v_cache, q_pos, out, k_scale, v_scale, lse, stream=stream)
+
+
+class ChunkedPrefill:
+    """Chunked sparse prefill of one sequence through the query-union path.
+
+    For chunk c (queries at positions first_c .. first_c + n_c - 1, the cache then
+    holding first_c + n_c tokens): append the chunk's keys and values into the paged
+    cache, build its bitsets, groups and union tables from its TopK pages, and attend.
+    Preparation needs only the chunk's TopK IDs, so with ``overlap=True`` chunk c+1's
+    preparation runs on a second stream while chunk c attends (PageWeaver Fig. 6: the
+    online cost decides the net gain; QUILT hides preparation by pipelining it).  The
+    tables are double-buffered: preparing chunk c+2 waits until chunk c's attention is
+    done with its buffers.  Appends stay on the main stream after the previous chunk's
+    attention, since a chunk may share its first page with the previous one.
+    Both streams have the default priority.
+    """
+
+    def __init__(self, hq: int, hkv: int, d: int, n_pages: int, page_size: int, max_chunk: int,
+                 k: int, window: int = 64, max_group: int = 8, device="cuda"):
+        self.page_size = page_size
+        self.plans = [SparsePrefill(nq=max_chunk, hq=hq, hkv=hkv, d=d, n_pages=n_pages,
+                                    page_size=page_size, kv_len=n_pages * page_size, k=k,
+                                    window=window, max_group=max_group, device=device)
+                      for _ in range(2)]
+        self.max_chunk = max_chunk
+        self.side = torch.cuda.Stream(device=device)
+
+    def _plan_for(self, i: int, n: int) -> "SparsePrefill":
+        p = self.plans[i % 2]
+        if n == p.nq:
+            return p
+        # a shorter (last) chunk: a plan of its own size on the same buffers' device
+        return SparsePrefill(nq=n, hq=p.hq, hkv=p.hkv, d=p.d, n_pages=p.n_pages, page_size=p.page_size,
+                             kv_len=p.kv_len, k=p.k, window=p.window, max_group=p.max_group,
+                             device=p.device)
+
+    def run(self, chunks, k_cache, v_cache, k_scale=None, v_scale=None, overlap: bool = True,
+            stream=None) -> None:
+        """chunks: sequence of dicts with q [n, hq, d] bf16, k_new / v_new [n, hkv, d] bf16,
+        topk [n, hkv, k] int32, q_pos [n] int32, out [n, hq, d] bf16, optional lse
+        [n, hq] fp32, and first_token (the chunk's first position)."""
+        main = torch.cuda.current_stream() if stream is None else stream
+        side = self.side if overlap else main
+        plans = [self._plan_for(i, c["q"].shape[0]) for i, c in enumerate(chunks)]
+        prepared = [torch.cuda.Event() for _ in chunks]
+        attended = [torch.cuda.Event() for _ in chunks]
+
+        def prepare(i):
+            if overlap:
+                if i == 0:
+                    side.wait_stream(main)              # inputs written earlier on the main stream
+                elif i >= 2:
+                    side.wait_event(attended[i - 2])   # chunk i-2 is done with these buffers
+            plans[i].prepare(chunks[i]["topk"], side)
+            prepared[i].record(side)
+
+        if chunks:
+            prepare(0)
+        for i, c in enumerate(chunks):
+            n = c["q"].shape[0]
+            pw_append_kv(c["k_new"], c["v_new"], c["first_token"], k_cache, v_cache, k_scale, v_scale,
+                         stream=main)
+            if i + 1 < len(chunks) and overlap:
+                prepare(i + 1)
+            main.wait_event(prepared[i])
+            plans[i].attend(c["q"], k_cache, v_cache, c["q_pos"], c["out"], k_scale, v_scale,
+                            c.get("lse"), stream=main, kv_len=c["first_token"] + n)
+            attended[i].record(main)
+            if i + 1 < len(chunks) and not overlap:
+                prepare(i + 1)
+        if overlap:
+            main.wait_stream(side)   # later work (and buffer reuse) follows every preparation

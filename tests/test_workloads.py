@@ -41,3 +41,15 @@ def test_supports_are_causal(name):
     w = make_workload(cfg)
     own = w.q_pos // cfg.ps
     assert (w.topk.max(axis=2) <= own[:, None]).all()
+
+
+def test_make_supports_draws_the_workloads_supports():
+    from workloads import make_supports
+    for name in ("c1_tiny", "c4_block_union"):
+        cfg = CONFIGS[name].scaled(kv_len=CONFIGS[name].kv_len // 4, nq=CONFIGS[name].nq // 4) \
+            if name == "c4_block_union" else CONFIGS[name]
+        w = make_workload(cfg)
+        q_pos, topk, rows = make_supports(cfg)
+        assert np.array_equal(q_pos, w.q_pos)
+        assert (topk is None and w.topk is None) or np.array_equal(topk, w.topk)
+        assert (rows is None and w.mask_rows is None) or np.array_equal(rows, w.mask_rows)

@@ -7,6 +7,6 @@ method's arithmetic (no bitsets, grouping, unions or attention), so both the
 CPU oracle and the HIP path may consume what it returns.
 """
 from .configs import CONFIGS, Config, get_config
-from .gen import Workload, make_workload
+from .gen import Workload, make_supports, make_workload
 
-__all__ = ["CONFIGS", "Config", "get_config", "Workload", "make_workload"]
+__all__ = ["CONFIGS", "Config", "get_config", "Workload", "make_supports", "make_workload"]

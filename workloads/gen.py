@@ -153,13 +153,11 @@ def _block_union_rows(cfg: Config, r_comm, r_picks) -> np.ndarray:
     return out
 
 
-def make_workload(cfg: Config, seed: Optional[int] = None) -> Workload:
-    seed = cfg.seed if seed is None else seed
-    if cfg.hq % cfg.hkv:
-        raise ValueError("hq must be a multiple of hkv")
-    r_comm, r_assign, r_picks, r_q, r_k, r_v = [
-        np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(6)]
-    q_pos = np.arange(cfg.first_pos, cfg.kv_len, dtype=np.int32)
+def _streams(seed: int):
+    return [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(6)]
+
+
+def _supports(cfg: Config, q_pos, r_comm, r_assign, r_picks):
     topk = mask_rows = None
     if cfg.support == "community":
         topk = _community_supports(cfg, q_pos, r_comm, r_assign, r_picks)
@@ -169,6 +167,24 @@ def make_workload(cfg: Config, seed: Optional[int] = None) -> Workload:
         mask_rows = _block_union_rows(cfg, r_comm, r_picks)
     else:
         raise ValueError(f"support {cfg.support!r}")
+    return topk, mask_rows
+
+
+def make_supports(cfg: Config, seed: Optional[int] = None):
+    """(q_pos, topk, mask_rows) exactly as make_workload draws them, without Q, K and V."""
+    seed = cfg.seed if seed is None else seed
+    r_comm, r_assign, r_picks, _, _, _ = _streams(seed)
+    q_pos = np.arange(cfg.first_pos, cfg.kv_len, dtype=np.int32)
+    return (q_pos,) + _supports(cfg, q_pos, r_comm, r_assign, r_picks)
+
+
+def make_workload(cfg: Config, seed: Optional[int] = None) -> Workload:
+    seed = cfg.seed if seed is None else seed
+    if cfg.hq % cfg.hkv:
+        raise ValueError("hq must be a multiple of hkv")
+    r_comm, r_assign, r_picks, r_q, r_k, r_v = _streams(seed)
+    q_pos = np.arange(cfg.first_pos, cfg.kv_len, dtype=np.int32)
+    topk, mask_rows = _supports(cfg, q_pos, r_comm, r_assign, r_picks)
     q = _to_bf16_bits(r_q.standard_normal((cfg.nq, cfg.hq, cfg.d), dtype=np.float32))
     k, k_scale = _kv_tensor(r_k, cfg)
     v, v_scale = _kv_tensor(r_v, cfg)
