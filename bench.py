@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3_long_fp8")
     ap.add_argument("--window", type=int, default=None)
+    ap.add_argument("--item-rows", type=int, default=None,
+                    help="block-union workloads: query-head rows per work item over the shared table")
     ap.add_argument("--flush-steps", type=int, default=20,
                     help="extra steps timed one by one after writing 512 MiB (L2/MALL flush)")
     ap.add_argument("--cpu-queries", type=int, default=4096,
@@ -145,6 +147,8 @@ def main():
     cfg = CONFIGS[args.workload]
     if args.window:
         cfg = cfg.scaled(window=args.window)
+    if args.item_rows:
+        cfg = cfg.scaled(item_rows=args.item_rows)
     w = make_workload(cfg)
     dev = torch.device("cuda:0")
 
