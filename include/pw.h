@@ -217,6 +217,30 @@ pw_status pw_sparse_prefill(const void* q, int nq, int hq, int hkv, int d,
                             const int32_t* union_pages, const uint8_t* union_qmask,
                             int64_t capacity, void* out, float* lse, hipStream_t stream);
 
+/* ---- (4b) shared block tables with the table split across workgroups ---------------------
+ * CompactAttention "Approach": with one block table per KV group (shared_table = 1 of
+ * pw_sparse_prefill, consecutive groups, every member using every page of the table) the
+ * work is dense paged attention, and a chunk has few query-head rows per KV group (a
+ * 1024-query chunk: 256 work items of 128 rows), too few to fill the chip.  Here table g
+ * is cut into n_split consecutive slices, one workgroup each, and the slices' partial
+ * results - normalised rows and their lse, in partial row ((q*hkv + g)*n_split + s)*G +
+ * (h - g*G) - are merged by lse into out / lse.  The result is the attention of
+ * pw_sparse_prefill(shared_table = 1, group_qids = NULL, union_qmask = NULL).
+ * Arguments as in pw_sparse_prefill; max_group as there (consecutive groups of
+ * max_group queries, ceil(nq / max_group) groups).  n_split = 1 is pw_sparse_prefill
+ * itself (partial buffers unused).
+ * partial_o    workspace bf16 [nq*hq*n_split][d]
+ * partial_lse  workspace fp32 [nq*hq*n_split]
+ * Limits: as pw_sparse_prefill's wide form; 1 <= n_split <= 64.                           */
+pw_status pw_shared_table_prefill(const void* q, int nq, int hq, int hkv, int d,
+                                  const void* k_cache, const void* v_cache, int kv_dtype,
+                                  const float* k_scale, const float* v_scale, int page_size,
+                                  int n_pages, int64_t stride_head, int64_t stride_page,
+                                  const int32_t* q_pos, int kv_len, float sm_scale, int max_group,
+                                  const int32_t* union_off, const int32_t* union_pages,
+                                  int64_t capacity, int n_split, void* partial_o,
+                                  float* partial_lse, void* out, float* lse, hipStream_t stream);
+
 /* ---- (5) direct KV-page union (page-major execution) -----------------------------------
  * PageWeaver abstract: the page-major alternative to query unions visits every
  * (KV head, page) once for all queries that selected it, and pays for it with

@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
             "pw_prepare": (I, [P, I, I, I, I, I, I, P, P, P, P, P, P, P, I64, P]),
             "pw_sparse_prefill": (I, [P, I, I, I, I, P, P, I, P, P, I, I, I64, I64, P, I, F,
                                       P, P, I, I, I, P, P, P, I64, P, P, P]),
+            "pw_shared_table_prefill": (I, [P, I, I, I, I, P, P, I, P, P, I, I, I64, I64, P, I, F,
+                                            I, P, P, I64, I, P, P, P, P, P]),
             "pw_page_items_capacity": (I64, [I, I, I, I, I]),
             "pw_page_workspace_bytes": (ctypes.c_size_t, [I, I, I]),
             "pw_page_tables": (I, [P, I, I, I, I, I, P, ctypes.c_size_t, P, P, P, P, P, P, I64, P]),
@@ -275,6 +277,29 @@ def _cache_dtype(k_cache: torch.Tensor) -> int:
     raise ValueError(f"unsupported cache dtype {k_cache.dtype}")
 
 
+def pw_shared_table_prefill(q, k_cache, v_cache, q_pos, kv_len: int, union_off, union_pages, out, *,
+                            hkv: int, max_group: int, n_split: int, partial_o=None, partial_lse=None,
+                            k_scale=None, v_scale=None, sm_scale: Optional[float] = None, lse=None,
+                            stream=None) -> None:
+    """Attention of consecutive query groups over one shared table per KV head, each table
+    cut into n_split slices whose partial rows are merged by lse."""
+    nq, hq, d = q.shape
+    _, n_pages, page_size, _ = k_cache.shape
+    if n_split > 1 and (partial_o is None or partial_lse is None or partial_o.numel() < nq * hq * n_split * d
+                        or partial_lse.numel() < nq * hq * n_split):
+        raise ValueError("partial buffers too small for n_split")
+    sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    _check(lib().pw_shared_table_prefill(
+        _ptr(q, torch.bfloat16, "q"), nq, hq, hkv, d, _ptr(k_cache, name="k_cache"),
+        _ptr(v_cache, name="v_cache"), _cache_dtype(k_cache), _ptr(k_scale, torch.float32, "k_scale"),
+        _ptr(v_scale, torch.float32, "v_scale"), page_size, n_pages, n_pages * page_size * d,
+        page_size * d, _ptr(q_pos, torch.int32, "q_pos"), kv_len, sm, max_group,
+        _ptr(union_off, torch.int32, "union_off"), _ptr(union_pages, torch.int32, "union_pages"),
+        union_pages.numel(), n_split, _ptr(partial_o, torch.bfloat16, "partial_o"),
+        _ptr(partial_lse, torch.float32, "partial_lse"), _ptr(out, torch.bfloat16, "out"),
+        _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
 def pw_page_items_capacity(nq: int, hkv: int, k_max: int, n_pages: int, chunk: int) -> int:
     return lib().pw_page_items_capacity(nq, hkv, k_max, n_pages, chunk)
 
@@ -420,6 +445,8 @@ class SparsePrefill:
     grouping: str = "affinity"  # "affinity" or "original" (topk mode)
     n_rows: int = 0             # block_union: mask rows per KV head
     fused: bool = True          # topk/affinity mode: one pw_prepare call for the three steps
+    n_split: int = 0            # block_union mode: table slices per KV head (0: enough to
+                                # give every SIMD two waves; 1: no partials)
     device: str = "cuda"
 
     def __post_init__(self):
@@ -454,6 +481,15 @@ class SparsePrefill:
         else:
             self.group_rows = torch.arange(self.n_rows, **i32).view(1, 1, -1).repeat(self.hkv, 1, 1)
             self.group_qids = self.group_size = self.union_qmask = None
+            if self.n_split <= 0:
+                G = self.hq // self.hkv
+                waves = self.hkv * self.n_groups * max(1, -(-self.max_group * G // 32))
+                self.n_split = max(1, min(8, -(-2048 // waves)))
+            self.partial_o = self.partial_lse = None
+            if self.n_split > 1:
+                rows = self.nq * self.hq * self.n_split
+                self.partial_o = torch.empty((rows, self.d), dtype=torch.bfloat16, device=dev)
+                self.partial_lse = torch.empty(rows, dtype=torch.float32, device=dev)
 
     def prepare(self, ids: torch.Tensor, stream=None) -> None:
         """Bitsets, grouping and union tables from topk [nq, hkv, k] or mask rows [n_rows, hkv, k]."""
@@ -476,6 +512,13 @@ class SparsePrefill:
     def attend(self, q, k_cache, v_cache, q_pos, out, k_scale=None, v_scale=None, lse=None,
                sm_scale=None, stream=None, kv_len: Optional[int] = None) -> None:
         kv_len = self.kv_len if kv_len is None else kv_len
+        if self.mode == "block_union" and self.n_split > 1:
+            pw_shared_table_prefill(q, k_cache, v_cache, q_pos, kv_len, self.union_off, self.union_pages,
+                                    out, hkv=self.hkv, max_group=self.max_group, n_split=self.n_split,
+                                    partial_o=self.partial_o, partial_lse=self.partial_lse,
+                                    k_scale=k_scale, v_scale=v_scale, sm_scale=sm_scale, lse=lse,
+                                    stream=stream)
+            return
         pw_sparse_prefill(q, k_cache, v_cache, q_pos, kv_len, self.union_off, self.union_pages,
                           out, hkv=self.hkv, n_groups=self.n_groups, max_group=self.max_group,
                           group_qids=self.group_qids, group_size=self.group_size,

@@ -328,6 +328,104 @@ pw_status pw_page_union_prefill(const void* q, int nq, int hq, int hkv, int d, c
   return PW_OK;
 }
 
+// Host validation shared by the entry points that run the union attention kernel.
+static pw_status check_sparse_prefill(const pw::AttnArgs& a, const char* who) {
+  if (a.nq < 0 || a.hq < 1 || a.hkv < 1 || a.n_pages < 1 || a.n_groups < 0 || a.kv_len < 0 ||
+      a.capacity < 0)
+    return fail(PW_ERR_ARG, "%s: bad sizes nq=%d hq=%d hkv=%d n_pages=%d n_groups=%d kv_len=%d", who,
+                a.nq, a.hq, a.hkv, a.n_pages, a.n_groups, a.kv_len);
+  if (a.hq % a.hkv) return fail(PW_ERR_ARG, "%s: hq=%d not a multiple of hkv=%d", who, a.hq, a.hkv);
+  if (a.d != 64 && a.d != 128) return fail(PW_ERR_UNSUPPORTED, "%s: d=%d (64 or 128)", who, a.d);
+  if (a.page_size != 64 && a.page_size != 128)
+    return fail(PW_ERR_UNSUPPORTED, "%s: page_size=%d (64 or 128)", who, a.page_size);
+  if (a.kv_dtype != PW_KV_BF16 && a.kv_dtype != PW_KV_FP8_E4M3)
+    return fail(PW_ERR_UNSUPPORTED, "%s: kv_dtype=%d", who, a.kv_dtype);
+  // Member masks and explicit groups hold up to 8 members; consecutive groups over tables
+  // without member masks (every member uses every page) may be wider.
+  const bool wide_ok = a.group_qids == nullptr && a.union_qmask == nullptr;
+  if (a.max_group < 1 || a.max_group > (wide_ok ? 256 : 8))
+    return fail(PW_ERR_UNSUPPORTED, "%s: max_group=%d not in 1..%d", who, a.max_group,
+                wide_ok ? 256 : 8);
+  const int G = a.hq / a.hkv;
+  const int max_rows = wide_ok ? pw::max_rows_per_item(a.d, a.kv_dtype) : 64;
+  if ((int64_t)G * a.max_group > max_rows)
+    return fail(PW_ERR_UNSUPPORTED, "%s: (hq/hkv)*max_group=%d > %d", who, G * a.max_group, max_rows);
+  if (a.shared_table != 0 && a.shared_table != 1)
+    return fail(PW_ERR_ARG, "%s: shared_table=%d (0 or 1)", who, a.shared_table);
+  const int esz = a.kv_dtype == PW_KV_FP8_E4M3 ? 1 : 2;
+  if (a.stride_page < (int64_t)a.page_size * a.d || a.stride_head < 0)
+    return fail(PW_ERR_ARG, "%s: stride_page=%lld < page_size*d or stride_head < 0", who,
+                (long long)a.stride_page);
+  if ((a.stride_page * esz) % 16 || (a.stride_head * esz) % 16)
+    return fail(PW_ERR_ARG, "%s: strides must be multiples of 16 bytes", who);
+  if (((uintptr_t)a.q | (uintptr_t)a.k_cache | (uintptr_t)a.v_cache | (uintptr_t)a.out) % 16)
+    return fail(PW_ERR_ARG, "%s: q, caches and out must be 16-byte aligned", who);
+  if (!a.group_qids && a.n_groups * (int64_t)a.max_group < a.nq)
+    return fail(PW_ERR_ARG, "%s: consecutive groups need n_groups*max_group >= nq", who);
+  if ((int64_t)a.hkv * a.n_groups >= INT32_MAX / 8)
+    return fail(PW_ERR_UNSUPPORTED, "%s: too many work items", who);
+  if (!(a.sm_scale > 0.f) || a.sm_scale != a.sm_scale)
+    return fail(PW_ERR_ARG, "%s: sm_scale must be positive", who);
+  if (a.nq > 0 && a.n_groups > 0) {
+    if (!a.q || !a.k_cache || !a.v_cache || !a.q_pos || !a.union_off || !a.out)
+      return fail(PW_ERR_ARG, "%s: null required pointer", who);
+    if (a.group_qids && !a.group_size)
+      return fail(PW_ERR_ARG, "%s: group_size is required with group_qids", who);
+    if (a.kv_dtype == PW_KV_FP8_E4M3 && (!a.k_scale || !a.v_scale))
+      return fail(PW_ERR_ARG, "%s: fp8 KV needs k_scale and v_scale", who);
+    if (a.capacity > 0 && !a.union_pages) return fail(PW_ERR_ARG, "%s: null union_pages", who);
+  }
+  return PW_OK;
+}
+
+pw_status pw_shared_table_prefill(const void* q, int nq, int hq, int hkv, int d,
+                                  const void* k_cache, const void* v_cache, int kv_dtype,
+                                  const float* k_scale, const float* v_scale, int page_size,
+                                  int n_pages, int64_t stride_head, int64_t stride_page,
+                                  const int32_t* q_pos, int kv_len, float sm_scale, int max_group,
+                                  const int32_t* union_off, const int32_t* union_pages,
+                                  int64_t capacity, int n_split, void* partial_o,
+                                  float* partial_lse, void* out, float* lse, hipStream_t stream) {
+  pw::g_err[0] = 0;
+  if (n_split < 1 || n_split > 64)
+    return fail(PW_ERR_UNSUPPORTED, "pw_shared_table_prefill: n_split=%d not in 1..64", n_split);
+  if (max_group < 1) return fail(PW_ERR_ARG, "pw_shared_table_prefill: max_group=%d", max_group);
+  const int n_groups = nq > 0 ? (nq + max_group - 1) / max_group : 0;
+  if (n_split == 1)
+    return pw_sparse_prefill(q, nq, hq, hkv, d, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                             page_size, n_pages, stride_head, stride_page, q_pos, kv_len, sm_scale,
+                             nullptr, nullptr, n_groups, max_group, 1, union_off, union_pages,
+                             nullptr, capacity, out, lse, stream);
+  if (hkv < 1 || hq < 1 || hq % hkv)
+    return fail(PW_ERR_ARG, "pw_shared_table_prefill: hq=%d hkv=%d", hq, hkv);
+  const int G = hq / hkv;
+  if ((int64_t)n_split * G > 16384)
+    return fail(PW_ERR_UNSUPPORTED, "pw_shared_table_prefill: n_split*(hq/hkv) > 16384");
+  if ((int64_t)nq * hkv * n_split >= INT32_MAX)
+    return fail(PW_ERR_UNSUPPORTED, "pw_shared_table_prefill: nq*hkv*n_split must stay below 2^31");
+  if ((int64_t)hkv * n_groups * n_split >= INT32_MAX / 8)
+    return fail(PW_ERR_UNSUPPORTED, "pw_shared_table_prefill: too many work items");
+  if (nq > 0 && (!partial_o || !partial_lse))
+    return fail(PW_ERR_ARG, "pw_shared_table_prefill: n_split > 1 needs partial_o and partial_lse");
+  if ((uintptr_t)partial_o % 16)
+    return fail(PW_ERR_ARG, "pw_shared_table_prefill: partial_o must be 16-byte aligned");
+  // the attention's own validation (wide consecutive groups over shared tables), writing
+  // the slice partials; then the lse merge into out / lse
+  pw::AttnArgs a{q, nq, hq, hkv, d, k_cache, v_cache, kv_dtype, k_scale, v_scale, page_size,
+                 n_pages, stride_head, stride_page, q_pos, kv_len, sm_scale, nullptr, nullptr,
+                 n_groups, max_group, 1, union_off, union_pages, nullptr, capacity, partial_o,
+                 partial_lse};
+  a.n_split = n_split;
+  const pw_status st = check_sparse_prefill(a, "pw_shared_table_prefill");
+  if (st != PW_OK || nq == 0) return st;
+  if (!out) return fail(PW_ERR_ARG, "pw_shared_table_prefill: null out");
+  if ((uintptr_t)out % 16) return fail(PW_ERR_ARG, "pw_shared_table_prefill: out must be 16-byte aligned");
+  const pw_status st2 = pw::launch_sparse_prefill(a, stream);
+  if (st2 != PW_OK) return st2;
+  return pw::launch_page_merge(nullptr, nq, hkv, 0, hkv, G, d, n_pages, n_split, partial_o,
+                               partial_lse, out, lse, stream);
+}
+
 pw_status pw_sparse_prefill(const void* q, int nq, int hq, int hkv, int d, const void* k_cache,
                             const void* v_cache, int kv_dtype, const float* k_scale,
                             const float* v_scale, int page_size, int n_pages, int64_t stride_head,
@@ -337,57 +435,12 @@ pw_status pw_sparse_prefill(const void* q, int nq, int hq, int hkv, int d, const
                             const int32_t* union_pages, const uint8_t* union_qmask,
                             int64_t capacity, void* out, float* lse, hipStream_t stream) {
   pw::g_err[0] = 0;
-  if (nq < 0 || hq < 1 || hkv < 1 || n_pages < 1 || n_groups < 0 || kv_len < 0 || capacity < 0)
-    return fail(PW_ERR_ARG, "pw_sparse_prefill: bad sizes nq=%d hq=%d hkv=%d n_pages=%d n_groups=%d kv_len=%d",
-                nq, hq, hkv, n_pages, n_groups, kv_len);
-  if (hq % hkv) return fail(PW_ERR_ARG, "pw_sparse_prefill: hq=%d not a multiple of hkv=%d", hq, hkv);
-  if (d != 64 && d != 128) return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: d=%d (64 or 128)", d);
-  if (page_size != 64 && page_size != 128)
-    return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: page_size=%d (64 or 128)", page_size);
-  if (kv_dtype != PW_KV_BF16 && kv_dtype != PW_KV_FP8_E4M3)
-    return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: kv_dtype=%d", kv_dtype);
-  // Member masks and explicit groups hold up to 8 members; consecutive groups over tables
-  // without member masks (every member uses every page) may be wider.
-  const bool wide_ok = group_qids == nullptr && union_qmask == nullptr;
-  if (max_group < 1 || max_group > (wide_ok ? 256 : 8))
-    return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: max_group=%d not in 1..%d", max_group,
-                wide_ok ? 256 : 8);
-  const int G = hq / hkv;
-  const int max_rows = wide_ok ? pw::max_rows_per_item(d, kv_dtype) : 64;
-  if ((int64_t)G * max_group > max_rows)
-    return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: (hq/hkv)*max_group=%d > %d", G * max_group,
-                max_rows);
-  if (shared_table != 0 && shared_table != 1)
-    return fail(PW_ERR_ARG, "pw_sparse_prefill: shared_table=%d (0 or 1)", shared_table);
-  const int esz = kv_dtype == PW_KV_FP8_E4M3 ? 1 : 2;
-  if (stride_page < (int64_t)page_size * d || stride_head < 0)
-    return fail(PW_ERR_ARG, "pw_sparse_prefill: stride_page=%lld < page_size*d or stride_head < 0",
-                (long long)stride_page);
-  if ((stride_page * esz) % 16 || (stride_head * esz) % 16)
-    return fail(PW_ERR_ARG, "pw_sparse_prefill: strides must be multiples of 16 bytes");
-  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) % 16)
-    return fail(PW_ERR_ARG, "pw_sparse_prefill: q, caches and out must be 16-byte aligned");
-  if (!group_qids && n_groups * (int64_t)max_group < nq)
-    return fail(PW_ERR_ARG, "pw_sparse_prefill: consecutive groups need n_groups*max_group >= nq");
-  if ((int64_t)hkv * n_groups >= INT32_MAX / 8)
-    return fail(PW_ERR_UNSUPPORTED, "pw_sparse_prefill: too many work items");
-  if (!(sm_scale > 0.f) || sm_scale != sm_scale)
-    return fail(PW_ERR_ARG, "pw_sparse_prefill: sm_scale must be positive");
-  const bool work = nq > 0 && n_groups > 0;
-  if (work) {
-    if (!q || !k_cache || !v_cache || !q_pos || !union_off || !out)
-      return fail(PW_ERR_ARG, "pw_sparse_prefill: null required pointer");
-    if (group_qids && !group_size)
-      return fail(PW_ERR_ARG, "pw_sparse_prefill: group_size is required with group_qids");
-    if (kv_dtype == PW_KV_FP8_E4M3 && (!k_scale || !v_scale))
-      return fail(PW_ERR_ARG, "pw_sparse_prefill: fp8 KV needs k_scale and v_scale");
-    if (capacity > 0 && !union_pages) return fail(PW_ERR_ARG, "pw_sparse_prefill: null union_pages");
-  }
-  if (!work) return PW_OK;
   pw::AttnArgs a{q, nq, hq, hkv, d, k_cache, v_cache, kv_dtype, k_scale, v_scale, page_size,
                  n_pages, stride_head, stride_page, q_pos, kv_len, sm_scale, group_qids, group_size,
                  n_groups, max_group, shared_table, union_off, union_pages, union_qmask, capacity,
                  out, lse};
+  const pw_status st = check_sparse_prefill(a, "pw_sparse_prefill");
+  if (st != PW_OK || nq == 0 || n_groups == 0) return st;
   return pw::launch_sparse_prefill(a, stream);
 }
 

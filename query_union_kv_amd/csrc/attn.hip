@@ -85,6 +85,7 @@ struct Params {
   int nq, hq, hkv, G;
   int page_size, n_pages, kv_len;
   int n_groups, max_group, shared_table;
+  int n_split;             // > 1: each item's table is cut into n_split slices (partials)
   int n_items, items_per_xcd;
   float score_scale;       // sm_scale * log2(e)
 };
@@ -177,7 +178,10 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   }
   const int item_rel = (b & 7) * per_xcd + (b >> 3);
   if (item_rel >= n_items) return;
-  const int item = item0 + item_rel;
+  const int item_s = item0 + item_rel;
+  // table slices: item_s = item * n_split + slice (consecutive slices share an XCD's L2)
+  const int slice = p.n_split > 1 ? item_s % p.n_split : 0;
+  const int item = p.n_split > 1 ? item_s / p.n_split : item_s;
   const int g = p.item_kvh ? p.item_kvh[item] : item / p.n_groups;
   const int j = item - g * p.n_groups;
 
@@ -253,6 +257,11 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   }
   e_begin = min<int64_t>(max<int64_t>(e_begin, 0), p.capacity);
   e_end = min<int64_t>(e_end, p.capacity);
+  if (p.n_split > 1) {   // this item's slice of the table
+    const int64_t per = (max<int64_t>(e_end - e_begin, 0) + p.n_split - 1) / p.n_split;
+    e_begin = min<int64_t>(e_begin + per * slice, e_end);
+    e_end = min<int64_t>(e_begin + per, e_end);
+  }
   const int tpp_shift = p.page_size == 128 ? 2 : 1;          // log2(tiles per page)
   const int n_tiles = (int)max<int64_t>(e_end - e_begin, 0) << tpp_shift;
 
@@ -510,8 +519,11 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   for (int m = 0; m < MT; ++m) {
     if (qid[m] < 0) continue;
     const float inv = l_run[m] > 0.f ? 1.0f / l_run[m] : 0.f;
-    const int64_t orow = p.out_slot ? (int64_t)slot[m] * p.G + (hh[m] - g * p.G)
-                                    : (int64_t)qid[m] * p.hq + hh[m];
+    int64_t orow = (int64_t)qid[m] * p.hq + hh[m];
+    if (p.out_slot)          // page-major partial slot
+      orow = (int64_t)slot[m] * p.G + (hh[m] - g * p.G);
+    else if (p.n_split > 1)  // table-slice partial: slot (q, g, slice)
+      orow = (((int64_t)qid[m] * p.hkv + g) * p.n_split + slice) * p.G + (hh[m] - g * p.G);
     uint16_t* dst = p.out + orow * D;
 #pragma unroll
     for (int dt = 0; dt < C::kDt; ++dt) {
@@ -604,7 +616,8 @@ pw_status launch_sparse_prefill(const AttnArgs& a, hipStream_t stream) {
   p.n_groups = a.n_groups;
   p.max_group = a.max_group;
   p.shared_table = a.shared_table;
-  p.n_items = a.item_kvh ? a.n_groups : a.hkv * a.n_groups;   // page-major: capacity
+  p.n_split = a.n_split;
+  p.n_items = a.item_kvh ? a.n_groups : a.hkv * a.n_groups * a.n_split;   // page-major: capacity
   p.items_per_xcd = (p.n_items + 7) / 8;
   p.score_scale = a.sm_scale * kLog2e;
   if (p.n_items == 0) return PW_OK;

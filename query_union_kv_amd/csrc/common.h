@@ -81,6 +81,10 @@ struct AttnArgs {
   // one page union_pages[i]; the items [*item_lo_dev, *item_hi_dev) run (n_groups bounds
   // their count); member j's row goes to partial row out_slot[i * max_group + j] * G +
   // (h - g*G).
+  // > 1: the table of every item is cut into n_split consecutive slices, one workgroup
+  // each; row (q, h) of slice s goes to partial row ((q*hkv + g)*n_split + s)*G + (h - g*G)
+  // of out/lse (merged afterwards by launch_page_merge with bits == NULL).
+  int n_split = 1;
   const int32_t* item_kvh = nullptr;
   const int32_t* item_lo_dev = nullptr;
   const int32_t* item_hi_dev = nullptr;

@@ -183,7 +183,8 @@ __global__ void k_fill_i32(int32_t* __restrict__ p, int n, int v) {
 }
 
 // One wave per (query, KV head).  Row (q, h) has partials at slots
-// (q * hkv + g) * k_max + r, r < min(|S(q, g)|, k_max); partial row = slot * G + (h - gG).
+// (q * hkv + g) * k_max + r, r < min(|S(q, g)|, k_max) (r < k_max when bits is NULL);
+// partial row = slot * G + (h - gG).
 //   lse = log sum_r exp(lse_r),  out = sum_r exp(lse_r - lse) * o_r
 // Rows without usable keys (every lse_r = -inf, or no partials) get 0 and -inf.
 // Dynamic LDS: k_max * G floats per wave (the weights).
@@ -197,10 +198,13 @@ __global__ __launch_bounds__(64) void k_page_merge(
   const int qg = blockIdx.x;                   // KV heads g0 .. g0 + hb - 1
   const int q = qg / hb, g = g0 + (qg - q * hb);
   if (q >= nq) return;
-  const uint64_t* row = bits + ((int64_t)g * nq + q) * words;
-  int n = 0;
-  for (int w = lane; w < words; w += kWave) n += __popcll(row[w]);
-  n = min(wave_sum(n), k_max);
+  int n = k_max;            // bits == NULL: every one of the k_max slots holds a partial
+  if (bits) {
+    const uint64_t* row = bits + ((int64_t)g * nq + q) * words;
+    n = 0;
+    for (int w = lane; w < words; w += kWave) n += __popcll(row[w]);
+    n = min(wave_sum(n), k_max);
+  }
   const int64_t slot0 = ((int64_t)q * hkv + g) * k_max;
   const int hq = hkv * G;
   for (int i = lane; i < n * G; i += kWave) wts[i] = part_lse[slot0 * G + i];

@@ -217,3 +217,26 @@ def test_page_union_validation(kw, code):
 
 def test_page_union_nothing_to_do_is_ok():
     assert _page_attn(nq=0)[0] == 0
+
+
+def _shared(**kw):
+    a = dict(q=NULL, nq=8, hq=4, hkv=1, d=128, k=NULL, v=NULL, kv_dtype=0, ks=NULL, vs=NULL, ps=64,
+             n_pages=4, sh=4 * 64 * 128, sp=64 * 128, q_pos=NULL, kv_len=256, sm=0.088, mg=8,
+             off=NULL, pages=NULL, cap=4, n_split=2, po=NULL, pl=NULL, out=NULL, lse=NULL, stream=NULL)
+    a.update(kw)
+    return _err(L.pw_shared_table_prefill(*a.values()))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_split=0), -2), (dict(n_split=65), -2), (dict(mg=0), -1),
+    (dict(), -1),                                   # no partial buffers for n_split > 1
+    (dict(po=16, pl=16, d=96), -2),                 # the attention's own checks
+    (dict(po=16, pl=16, hq=64, mg=8), -2),          # 512 rows per work item
+])
+def test_shared_table_validation(kw, code):
+    st, msg = _shared(**kw)
+    assert st == code and msg.startswith(("pw_shared_table_prefill", "pw_sparse_prefill")), msg
+
+
+def test_shared_table_nothing_to_do_is_ok():
+    assert _shared(nq=0, po=16, pl=16)[0] == 0

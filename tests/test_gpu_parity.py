@@ -168,3 +168,28 @@ def test_fused_prepare_equals_separate_steps(kw):
     for key in ("bits", "group_qids", "group_size", "union_off", "union_pages", "union_qmask", "out"):
         assert np.array_equal(a[key], b[key]), key
     _compare_tables(a, oracle_tables(w))
+
+
+@pytest.mark.parametrize("n_split", [1, 2, 3, 7])
+def test_block_union_table_slices(n_split):
+    """Shared per-KV-group tables cut into n_split slices (partials merged by lse) give the
+    attention of the whole table."""
+    from gpu_util import make_plan, device_inputs
+    cfg = CONFIGS["c4_block_union"].scaled(kv_len=16384, nq=256, seed=44)
+    print(f"[parity] block-union slices n_split={n_split}", flush=True)
+    w = make_workload(cfg)
+    d = device_inputs(w)
+    plan = make_plan(w)
+    plan_split = type(plan)(**{**{f: getattr(plan, f) for f in ("nq", "hq", "hkv", "d", "n_pages", "page_size",
+                                                              "kv_len", "k", "window", "max_group", "mode",
+                                                              "grouping", "n_rows", "fused")},
+                               "n_split": n_split})
+    assert plan_split.n_split == n_split
+    out = torch.full_like(d["q"], float("nan"))
+    lse = torch.full(d["q"].shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+    plan_split(d["ids"], d["q"], d["k"], d["v"], d["q_pos"], out, d["k_scale"], d["v_scale"], lse)
+    torch.cuda.synchronize()
+    ref = oracle_tables(w)
+    O, L = oracle_attention(w, ref["S"])
+    check_close(out.float().cpu().numpy(), O, cfg.kv_dtype, f"n_split={n_split}")
+    check_lse(lse.cpu().numpy(), L, f"n_split={n_split}")
