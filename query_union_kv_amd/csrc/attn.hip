@@ -114,15 +114,14 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 v) {
 // voff per lane): lane l's bytes land at LDS address lds + 16*l.  M0 carries the LDS
 // address and is restored afterwards.
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
-  uint32_t saved;
+  // M0 holds the LDS destination; it is declared clobbered, so the compiler restores
+  // whatever it keeps there itself
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
       : "v"(voff), "s"(sbase), "s"(lds)
-      : "memory");
+      : "memory", "m0");
 }
 
 template <int N>
@@ -390,7 +389,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     }
     const float sc = p.score_scale * ks;                      // log2-domain score scale
     const float lvs = FP8 ? __builtin_amdgcn_logf(vs) : 0.f;  // log2 of the V page scale
-    const float inv_vs = FP8 ? 1.0f / vs : 1.f;
+    // 1 / vs only scales the row sums, so the hardware reciprocal (1 ulp) is ample
+    const float inv_vs = FP8 ? __builtin_amdgcn_rcpf(vs) : 1.f;
     const PW_LDS uint8_t* st = lds_p + SS * C::kStageBytes;
 
     // K fragments (A operand of S^T = K . Q^T), shared by every row tile
@@ -423,33 +423,45 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
       const bool sel = (qm & my_bit[m]) != 0;
       const bool row_any = sel && tok0 <= row_lim[m];
       const bool tile_full = tok0 + kTK - 1 <= mt_min[m];          // uniform
-      auto scores = [&](float bias, float* x) {
+      // scores in the log2 domain; keys after a row's last usable token -> -inf.  A tile
+      // wholly before every row's limit (the common case) needs no causal compare.
+      auto scores = [&](float bias, float* x, auto masked_c) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
             float v = __builtin_fmaf(s2[kb][ii], sc, bias);
-            if (!tile_full && tok0 + 8 * lq + 4 * kb + ii > row_lim[m]) v = -INFINITY;
+            if constexpr (decltype(masked_c)::value)
+              if (tok0 + 8 * lq + 4 * kb + ii > row_lim[m]) v = -INFINITY;
             x[4 * kb + ii] = v;
           }
       };
       // fast path: P = exp2(s*sc - reference + log2 vs) with the current reference
       float pv[8];
-      scores(sel && m_ref[m] != -INFINITY ? lvs - m_ref[m] : -INFINITY, pv);
+      const float bias0 = sel && m_ref[m] != -INFINITY ? lvs - m_ref[m] : -INFINITY;
+      if (tile_full)
+        scores(bias0, pv, std::false_type{});
+      else
+        scores(bias0, pv, std::true_type{});
+      // this lane's share of the row sum (its 8 of the tile's 32 keys); the four lanes of a
+      // row are added up once, in the epilogue
       float lsum = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         pv[k] = __builtin_amdgcn_exp2f(pv[k]);
         lsum += pv[k];
       }
-      lsum += __shfl_xor(lsum, 16, kWave);
-      lsum += __shfl_xor(lsum, 32, kWave);
-      // The reference must be set (first used tile of a row) or raised (a row sum passed
-      // 2^kRescaleLog2, or overflowed): rare, wave-uniform slow path.
-      const bool need = row_any && (m_ref[m] == -INFINITY || !(lsum * inv_vs <= 0x1p32f));
-      if (__builtin_amdgcn_ballot_w64(need)) {
+      // The reference must be set (first used tile of a row) or raised (a lane's share of a
+      // row sum passed 2^30, or overflowed): rare, wave-uniform slow path.  The decision is
+      // made per row - lanes li, li+16, li+32 and li+48 hold row li - so that every key of
+      // a row is exponentiated against the same reference.
+      const bool need_lane = row_any && (m_ref[m] == -INFINITY || !(lsum * inv_vs <= 0x1p30f));
+      const uint64_t nb = __builtin_amdgcn_ballot_w64(need_lane);
+      if (nb) {
+        const uint32_t rows = (uint32_t)(nb | (nb >> 16) | (nb >> 32) | (nb >> 48)) & 0xFFFFu;
+        const bool need = (rows >> li) & 1u;
         float raw[8];
-        scores(sel ? 0.f : -INFINITY, raw);
+        scores(sel ? 0.f : -INFINITY, raw, std::true_type{});
         float mloc = -INFINITY;
 #pragma unroll
         for (int k = 0; k < 8; ++k) mloc = fmaxf(mloc, raw[k]);
@@ -468,8 +480,6 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
           pv[k] = __builtin_amdgcn_exp2f(raw[k] + bias);
           lsum += pv[k];
         }
-        lsum += __shfl_xor(lsum, 16, kWave);
-        lsum += __shfl_xor(lsum, 32, kWave);
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) pf[m][k] = (__bf16)pv[k];
@@ -515,6 +525,11 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   wait_vmcnt<0>();
 
   // ---- epilogue: rows to their original IDs ------------------------------------------
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {   // the row sums: add the four lanes' shares of each row
+    l_run[m] += __shfl_xor(l_run[m], 16, kWave);
+    l_run[m] += __shfl_xor(l_run[m], 32, kWave);
+  }
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     if (qid[m] < 0) continue;
