@@ -41,7 +41,9 @@ def parse():
     ap.add_argument("--item-rows", type=int, default=None,
                     help="block-union workloads: query-head rows per work item over the shared table")
     ap.add_argument("--flush-steps", type=int, default=20,
-                    help="extra steps timed one by one after writing 512 MiB (L2/MALL flush)")
+                    help="replays per round, each timed after writing 512 MiB (L2/MALL flush)")
+    ap.add_argument("--flush-rounds", type=int, default=7,
+                    help="rounds of flushed replays (median of the round medians is reported)")
     ap.add_argument("--cpu-queries", type=int, default=4096,
                     help="oracle sample: the first N queries (whole windows), all KV heads")
     ap.add_argument("--no-cpu", action="store_true")
@@ -249,7 +251,23 @@ def main():
         torch.cuda.synchronize()
         orig_pages = int(orig.union_off[-1].item())
         per_q = cfg.nq * cfg.hkv
+        # useful work: keys each (query, head) row actually uses, |J| = sum over its support
+        # pages of the tokens at or before its position and before the cache end
+        tk = np.asarray(ids_np, dtype=np.int64)                            # [nq, hkv, K]
+        valid = (tk >= 0) & (tk < cfg.n_pages)
+        uniq = np.where(valid, tk, -1)
+        uniq = np.sort(uniq, axis=2)
+        first = np.concatenate([np.ones_like(uniq[:, :, :1], dtype=bool), uniq[:, :, 1:] != uniq[:, :, :-1]], axis=2)
+        keep = first & (uniq >= 0)
+        lim = np.minimum(w.q_pos.astype(np.int64)[:, None, None] + 1, cfg.kv_len)
+        used = np.clip(lim - uniq * cfg.ps, 0, cfg.ps) * keep
+        keys_used = int(used.sum()) * cfg.g                                # over all query heads
+        useful_flops = 4.0 * cfg.d * keys_used
+        page_bytes = cfg.ps * cfg.d * (1 if cfg.kv_dtype == "fp8" else 2) * 2 + (8 if cfg.kv_dtype == "fp8" else 0)
         extras.update({
+            "useful_tflops": useful_flops / (attn_ms / 1e3) / 1e12,
+            "bytes": {"B_u": Bu, "B_query": selected * page_bytes, "B_orig": orig_pages * page_bytes,
+                      "B_distinct": int(len(np.unique(np.nonzero(keep)[1] * cfg.n_pages + uniq[keep]))) * page_bytes},
             "visits_per_query_kvh": {"per_query": selected / per_q, "original_union": orig_pages / per_q,
                                      "affinity_union": total_pages / per_q},
             "masked_slot_frac": (slots - selected) / slots if slots else 0.0,
@@ -350,20 +368,28 @@ def main():
             "queries_per_s_overlapped": cfg.kv_len / (t_ovl / 1e3)}
         del kc3, vc3, ks3, vs3, chunk_list, runner
 
-    # ---- flushed timing: 512 MiB written before each step, outside the event pair ----------
+    # ---- flushed timing: rounds of replays, 512 MiB written before each replay outside the
+    # event pair; the median of the round medians and their range ---------------------------
     if args.flush_steps:
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        fl = []
-        for _ in range(args.flush_steps):
-            scratch.fill_(1)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            step(e)
-            torch.cuda.synchronize()
-            fl.append((e[0].elapsed_time(e[2]), e[1].elapsed_time(e[2])))
+        rounds = []
+        for _ in range(max(1, args.flush_rounds)):
+            fl = []
+            for _ in range(args.flush_steps):
+                scratch.fill_(1)
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                step(e)
+                torch.cuda.synchronize()
+                fl.append((e[0].elapsed_time(e[2]), e[1].elapsed_time(e[2])))
+            rounds.append((statistics.median(x[0] for x in fl), statistics.median(x[1] for x in fl)))
         del scratch
-        f_call = statistics.median(x[0] for x in fl)
-        f_attn = statistics.median(x[1] for x in fl)
-        extras["flushed"] = {"ms_per_call_median": f_call, "attn_ms_median": f_attn,
+        f_call = statistics.median(r[0] for r in rounds)
+        f_attn = statistics.median(r[1] for r in rounds)
+        extras["flushed"] = {"rounds": len(rounds), "replays_per_round": args.flush_steps,
+                             "ms_per_call_median": f_call, "ms_per_call_range": [min(r[0] for r in rounds),
+                                                                                 max(r[0] for r in rounds)],
+                             "attn_ms_median": f_attn, "attn_ms_range": [min(r[1] for r in rounds),
+                                                                         max(r[1] for r in rounds)],
                              "queries_per_s": cfg.nq / (f_call / 1e3),
                              "unique_kv_GBs": Bu / (f_attn / 1e3) / 1e9}
 
