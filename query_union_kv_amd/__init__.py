@@ -602,3 +602,28 @@ class ChunkedPrefill:
                 prepare(i + 1)
         if overlap:
             main.wait_stream(side)   # later work (and buffer reuse) follows every preparation
+
+
+def sparse_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, topk: torch.Tensor,
+                   q_pos: torch.Tensor, *, kv_len: int, k_scale: Optional[torch.Tensor] = None,
+                   v_scale: Optional[torch.Tensor] = None, window: int = 64, max_group: int = 8,
+                   sm_scale: Optional[float] = None, with_lse: bool = False, stream=None):
+    """One complete query-union call on the current stream: bitsets, affinity grouping and
+    union tables from topk [nq, hkv, K], then attention.  q bf16 [nq, hq, d]; caches
+    [hkv, n_pages, page_size, d] (bf16, or uint8 e4m3fn codes with fp32 scales
+    [hkv, n_pages]).  Returns (out, aux): out bf16 [nq, hq, d]; aux holds the plan with
+    its bitsets, groups and union tables, and lse [nq, hq] when with_lse."""
+    nq, hq, d = q.shape
+    hkv, n_pages, page_size, _ = k_cache.shape
+    plan = SparsePrefill(nq=nq, hq=hq, hkv=hkv, d=d, n_pages=n_pages, page_size=page_size, kv_len=kv_len,
+                         k=topk.shape[2], window=window, max_group=max_group, device=q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty((nq, hq), dtype=torch.float32, device=q.device) if with_lse else None
+    plan.prepare(topk, stream)
+    plan.attend(q, k_cache, v_cache, q_pos, out, k_scale, v_scale, lse, sm_scale, stream)
+    aux = {"plan": plan, "bits": plan.bits, "group_qids": plan.group_qids, "group_size": plan.group_size,
+           "union_off": plan.union_off, "union_pages": plan.union_pages, "union_qmask": plan.union_qmask,
+           "bad_ids": plan.bad_ids}
+    if with_lse:
+        aux["lse"] = lse
+    return out, aux

@@ -304,7 +304,9 @@ __global__ __launch_bounds__(256) void k_prepare(const int32_t* __restrict__ top
                                                  int32_t* __restrict__ group_size,
                                                  int32_t* __restrict__ union_count) {
   __shared__ uint32_t rows[64][33];                    // +1 dword per row against bank conflicts
-  __shared__ int part[4][64];
+  // per-candidate partial scores of the (up to 4) waves, lane-major so that one 16-byte
+  // read gathers them; two buffers, alternating per pick, so one barrier per pick suffices
+  __shared__ __attribute__((aligned(16))) int part[2][64][4];
   __shared__ int red[4];
   const int g = blockIdx.y;
   const int start = blockIdx.x * window;
@@ -345,6 +347,10 @@ __global__ __launch_bounds__(256) void k_prepare(const int32_t* __restrict__ top
   uint64_t free_mask = __ballot(lane < len);
   const int64_t gbase = (int64_t)g * n_groups + (int64_t)blockIdx.x * (window / max_group);
   int gi = 0;
+  int pb = 0;   // partial-score buffer of the next pick
+  if (nwaves > 1)
+    for (int i = tid; i < 2 * 64 * 4; i += blockDim.x) (&part[0][0][0])[i] = 0;
+  __syncthreads();
   while (free_mask) {
     const int seed = __builtin_ctzll(free_mask);
     free_mask &= free_mask - 1;
@@ -364,10 +370,13 @@ __global__ __launch_bounds__(256) void k_prepare(const int32_t* __restrict__ top
         partial += __builtin_popcount(lo[i] & ulo[i]) + __builtin_popcount(hi[i] & uhi[i]);
       int score = partial;
       if (nwaves > 1) {
-        part[wave][lane] = partial;
+        // a wave rewrites buffer pb only two picks later, after every wave has passed the
+        // barrier of the pick in between (and so has read this pick's partials)
+        part[pb][lane][wave] = partial;
         __syncthreads();
-        score = 0;
-        for (int v = 0; v < nwaves; ++v) score += part[v][lane];
+        const int4 ps = *reinterpret_cast<const int4*>(&part[pb][lane][0]);
+        score = ps.x + ps.y + ps.z + ps.w;   // unused waves' slots stay 0
+        pb ^= 1;
       }
       const bool is_free = (free_mask >> lane) & 1ull;
       const int best = wave_max_dpp(is_free ? ((score << 6) | (63 - lane)) : -1);
@@ -381,7 +390,6 @@ __global__ __launch_bounds__(256) void k_prepare(const int32_t* __restrict__ top
 #pragma unroll
       for (int j = 1; j < 8; ++j) if (j == cnt) members[j] = pick;
       ++cnt;
-      if (nwaves > 1) __syncthreads();   // every wave has read `part` before it is rewritten
     }
     // union size: popcount of U over every wave's words
     int usz = 0;

@@ -193,3 +193,20 @@ def test_block_union_table_slices(n_split):
     O, L = oracle_attention(w, ref["S"])
     check_close(out.float().cpu().numpy(), O, cfg.kv_dtype, f"n_split={n_split}")
     check_lse(lse.cpu().numpy(), L, f"n_split={n_split}")
+
+
+def test_one_call_convenience_matches_oracle():
+    import query_union_kv_amd as pw
+    from gpu_util import device_inputs
+    cfg = _small(nq=130, k=8, kv_len=2048, hq=8, hkv=2, kv_dtype="fp8")
+    w = make_workload(cfg)
+    d = device_inputs(w)
+    out, aux = pw.sparse_prefill(d["q"], d["k"], d["v"], d["ids"], d["q_pos"], kv_len=cfg.kv_len,
+                                 k_scale=d["k_scale"], v_scale=d["v_scale"], window=cfg.window,
+                                 max_group=cfg.max_group, with_lse=True)
+    torch.cuda.synchronize()
+    ref = oracle_tables(w)
+    assert np.array_equal(aux["group_qids"].cpu().numpy(), ref["group_qids"])
+    O, L = oracle_attention(w, ref["S"])
+    check_close(out.float().cpu().numpy(), O, cfg.kv_dtype, "sparse_prefill")
+    check_lse(aux["lse"].cpu().numpy(), L, "sparse_prefill")
