@@ -24,6 +24,7 @@ the design notes):
 """
 from __future__ import annotations
 
+import itertools
 from typing import List, Sequence
 
 import numpy as np
@@ -248,3 +249,51 @@ def page_items_to_arrays(items, chunk: int):
         slots[i, :len(sl)] = sl
         size[i] = len(members)
     return kvh, pages, qids, slots, size
+
+
+# ---------------------------------------------------------------------------
+# cascaded sharing at row-tile granularity
+
+
+def arrange_for_tiles(bits_g: Sequence[int], members: Sequence[int], tile_members: int) -> List[int]:
+    """QUILT's cascaded sharing (summary, "Cascaded Sharing": pages shared by a whole
+    group, then sharing inside smaller subgroups) read at the granularity at which the
+    attention can skip work: a row tile of ``tile_members`` members.  For a group with
+    more members than one tile and at most two tiles' worth (tile_members = 4: 5..8
+    members), the members are split into a first tile that holds the seed (member 0)
+    and the rest, choosing the split with the smallest sum over the two tiles of
+    |union of the tile's supports|; ties go to the first split in the order of
+    ``itertools.combinations`` over the other members' positions.  Members keep their
+    relative order inside each tile.  Other shapes are returned unchanged."""
+    n = len(members)
+    if tile_members != 4 or n <= tile_members or n > 2 * tile_members:
+        return list(members)
+
+    def union_size(idx):
+        u = 0
+        for i in idx:
+            u |= bits_g[members[i]]
+        return bin(u).count("1")
+
+    best = None
+    for comb in itertools.combinations(range(1, n), tile_members - 1):
+        first = [0, *comb]
+        rest = [i for i in range(n) if i not in first]
+        cost = union_size(first) + union_size(rest)
+        if best is None or cost < best[0]:
+            best = (cost, first + rest)
+    return [members[i] for i in best[1]]
+
+
+def tile_activations(bits_g: Sequence[int], groups: List[List[int]], tile_members: int) -> int:
+    """Row tiles the attention computes for one KV head: for every group and every page
+    of its union, the tiles (runs of tile_members members in group order) of which at
+    least one member selected the page."""
+    total = 0
+    for members in groups:
+        for t in range(0, len(members), tile_members):
+            u = 0
+            for m in members[t:t + tile_members]:
+                u |= bits_g[m]
+            total += bin(u).count("1")
+    return total

@@ -61,6 +61,10 @@ MUTATIONS = [
      lambda: P.test_page_items_hand_trace()),
     (prep, "page_items", "range(0, len(qs), chunk)", "range(0, len(qs), chunk + 1)",
      lambda: P.test_page_items_cover_every_edge_once()),
+    (prep, "arrange_for_tiles", "cost < best[0]", "cost <= best[0]",
+     lambda: P.test_arrange_for_tiles_hand_trace()),
+    (prep, "arrange_for_tiles", "union_size(first) + union_size(rest)", "union_size(first)",
+     lambda: P.test_arrange_for_tiles_is_the_brute_force_minimum()),
     (kvcache, "e4m3fn_encode", "(hi % 2 == 0)", "(hi % 2 == 1)",
      lambda: K.test_encode_ties_go_to_even_code()),
     (kvcache, "quantize", "/ np.float32(scale)", "* np.float32(scale)",

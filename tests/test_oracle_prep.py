@@ -221,3 +221,34 @@ def test_page_items_cover_every_edge_once():
             assert 1 <= len(members) <= chunk and members == sorted(members)
             for q, s in zip(members, sl):
                 assert s == (q * c.hkv + g) * k_max + sorted(S[g][q]).index(p)
+
+
+def test_arrange_for_tiles_hand_trace():
+    # members 0..7; pages: 0,2,4,6 share page 10; 1,3,5,7 share page 11; everyone has page 0
+    bits = [(1 << 0) | (1 << (10 + (q % 2))) for q in range(8)]
+    members = list(range(8))
+    arr = prep.arrange_for_tiles(bits, members, 4)
+    assert arr == [0, 2, 4, 6, 1, 3, 5, 7]
+    assert prep.tile_activations(bits, [arr], 4) == 4            # {0,10} + {0,11}
+    assert prep.tile_activations(bits, [members], 4) == 6        # {0,10,11} twice
+    # ties (identical supports) keep the first split in combination order: no change
+    assert prep.arrange_for_tiles([5] * 8, members, 4) == members
+    # small groups and other tile sizes are left alone
+    assert prep.arrange_for_tiles(bits, [3, 1, 2], 4) == [3, 1, 2]
+    assert prep.arrange_for_tiles(bits, members, 2) == members
+
+
+def test_arrange_for_tiles_is_the_brute_force_minimum():
+    import itertools
+    rng = random.Random(3)
+    for n in range(5, 9):
+        for trial in range(20):
+            bits = [rng.getrandbits(24) & rng.getrandbits(24) for _ in range(n)]
+            members = list(range(n))
+            arr = prep.arrange_for_tiles(bits, members, 4)
+            assert sorted(arr) == members and arr[0] == 0
+            best = min(prep.tile_activations(bits, [[0, *c] + [i for i in range(1, n) if i not in c]], 4)
+                       for c in itertools.combinations(range(1, n), 3))
+            assert prep.tile_activations(bits, [arr], 4) == best
+            # relative order kept inside each tile
+            assert arr[:4] == sorted(arr[:4]) and arr[4:] == sorted(arr[4:])
