@@ -287,6 +287,23 @@ def main():
                              "online_cost": t_online - t_fixed, "net_saving": t_orig - t_online}
         exec_rows_pages = float((sizes * gsz).sum()) * cfg.g     # (row, union page) pairs
 
+        # Members arranged for 4-member row tiles (QUILT's cascaded sharing at row-tile
+        # granularity): row tiles computed, from the member masks, and attention time.
+        if cfg.g == 4 and cfg.max_group > 4:
+            arr = pw.SparsePrefill(nq=cfg.nq, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, n_pages=cfg.n_pages,
+                                   page_size=cfg.ps, kv_len=cfg.kv_len, k=ids.shape[2], window=cfg.window,
+                                   max_group=cfg.max_group, arrange=True, device=dev)
+            t_arr_prep = timed(lambda: arr.prepare(ids, stream))
+            t_arr_attn = timed(lambda: arr.attend(q, kc, vc, q_pos, out, ks, vs, stream=stream))
+
+            def tiles_of(plan_):
+                qm_ = plan_.union_qmask[:int(plan_.union_off[-1].item())].cpu().numpy()
+                return int(((qm_ & 0x0F) != 0).sum() + ((qm_ & 0xF0) != 0).sum())
+            extras["tile_arrangement"] = {
+                "row_tiles_pick_order": tiles_of(plan), "row_tiles_arranged": tiles_of(arr),
+                "prep_ms": t_arr_prep, "attn_ms": t_arr_attn, "attn_ms_pick_order": t_fixed}
+            del arr
+
         # The direct KV-page union on the same inputs: every (KV head, page) once,
         # per-page partials, lse merge (a separate entry point, compared here).
         pu = pw.PageUnionPrefill(nq=cfg.nq, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, n_pages=cfg.n_pages,

@@ -130,6 +130,27 @@ pw_status pw_page_bitsets(const int32_t* topk, int n_rows, int hkv, int k, int n
 pw_status pw_group(const uint64_t* bits, int nq, int hkv, int n_pages, int window,
                    int max_group, int32_t* group_qids, int32_t* group_size, hipStream_t stream);
 
+/* ---- (2b) members arranged for row tiles --------------------------------------------------
+ * QUILT summary, "Cascaded Sharing": after the pages shared by a whole group, reuse is
+ * sought inside smaller subgroups.  The attention skips work per row tile of 16 query-head
+ * rows, i.e. per subgroup of 16/(hq/hkv) members, so the subgroups that matter are the
+ * tiles: a page selected only inside one tile costs that tile alone.  For hq/hkv = 4 and
+ * groups of 5..8 members (two tiles), this reorders each group's members so that the split
+ * into [first 4 | rest] - the first tile holding the group's seed - has the smallest
+ * |union of tile 1| + |union of tile 2|, ties to the first split in lexicographic order of
+ * the seed's three partners' positions; each tile keeps its members' relative order.
+ * The member-mask bits of the group's union entries are permuted to match, so the tables
+ * stay consistent and the attention result is unchanged (bit for bit).  Other GQA ratios
+ * and smaller groups: no-op.
+ * bits, group_qids, group_size: as for pw_group (groups updated in place); union_off,
+ * union_qmask, capacity: the tables pw_union_tables / pw_prepare wrote for these groups
+ * (union_qmask updated in place; NULL: none).
+ * Limits: 1 <= max_group <= 8, n_pages <= 65536.                                            */
+pw_status pw_arrange_groups(const uint64_t* bits, int nq, int hkv, int n_pages, int hq,
+                            int n_groups, int max_group, int32_t* group_qids,
+                            const int32_t* group_size, const int32_t* union_off,
+                            uint8_t* union_qmask, int64_t capacity, hipStream_t stream);
+
 /* ---- (3) union tables -----------------------------------------------------------------
  * PageWeaver Fig. 2 (a group's union is visited once, members keep their own
  * pages) and CompactAttention "Approach" (Q-block and intra-group head unions

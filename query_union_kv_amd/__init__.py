@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
             "pw_page_bitsets": (I, [P, I, I, I, I, P, P, P]),
             "pw_group": (I, [P, I, I, I, I, I, P, P, P]),
             "pw_union_tables": (I, [P, I, I, I, P, P, I, I, I, P, P, P, I64, P]),
+            "pw_arrange_groups": (I, [P, I, I, I, I, I, I, P, P, P, P, I64, P]),
             "pw_prepare": (I, [P, I, I, I, I, I, I, P, P, P, P, P, P, P, I64, P]),
             "pw_sparse_prefill": (I, [P, I, I, I, I, P, P, I, P, P, I, I, I64, I64, P, I, F,
                                       P, P, I, I, I, P, P, P, I64, P, P, P]),
@@ -185,6 +186,21 @@ def pw_group(bits: torch.Tensor, n_pages: int, window: int, max_group: int,
     _check(lib().pw_group(_ptr(bits, torch.int64, "bits"), nq, hkv, n_pages, window, max_group,
                           _ptr(group_qids, torch.int32, "group_qids"),
                           _ptr(group_size, torch.int32, "group_size"), _stream(stream)))
+
+
+def pw_arrange_groups(bits: torch.Tensor, n_pages: int, hq: int, group_qids: torch.Tensor,
+                      group_size: torch.Tensor, union_off: torch.Tensor,
+                      union_qmask: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Reorders each group's members for 4-member row tiles (hq/hkv = 4, groups of 5..8) and
+    permutes its member-mask bits to match; a no-op for other shapes."""
+    hkv, nq, _ = bits.shape
+    _, n_groups, max_group = group_qids.shape
+    _check(lib().pw_arrange_groups(_ptr(bits, torch.int64, "bits"), nq, hkv, n_pages, hq, n_groups,
+                                   max_group, _ptr(group_qids, torch.int32, "group_qids"),
+                                   _ptr(group_size, torch.int32, "group_size"),
+                                   _ptr(union_off, torch.int32, "union_off"),
+                                   _ptr(union_qmask, torch.uint8, "union_qmask"),
+                                   union_qmask.numel() if union_qmask is not None else 0, _stream(stream)))
 
 
 def pw_union_tables(bits: torch.Tensor, n_pages: int, group_rows: torch.Tensor,
@@ -445,6 +461,7 @@ class SparsePrefill:
     grouping: str = "affinity"  # "affinity" or "original" (topk mode)
     n_rows: int = 0             # block_union: mask rows per KV head
     fused: bool = True          # topk/affinity mode: one pw_prepare call for the three steps
+    arrange: bool = False       # topk mode: members arranged for row tiles (pw_arrange_groups)
     n_split: int = 0            # block_union mode: table slices per KV head (0: enough to
                                 # give every SIMD two waves; 1: no partials)
     device: str = "cuda"
@@ -497,6 +514,9 @@ class SparsePrefill:
             pw_prepare(ids, self.n_pages, self.window, self.max_group, self.bits, self.group_qids,
                        self.group_size, self.union_off, self.union_pages, self.union_qmask,
                        self.bad_ids, stream)
+            if self.arrange:
+                pw_arrange_groups(self.bits, self.n_pages, self.hq, self.group_qids, self.group_size,
+                                  self.union_off, self.union_qmask, stream)
             return
         pw_page_bitsets(ids, self.n_pages, self.bits, self.bad_ids, stream)
         if self.mode == "topk":
@@ -505,6 +525,9 @@ class SparsePrefill:
                          self.group_size, stream)
             pw_union_tables(self.bits, self.n_pages, self.group_qids, self.group_size, self.k,
                             self.union_off, self.union_pages, self.union_qmask, stream)
+            if self.arrange:
+                pw_arrange_groups(self.bits, self.n_pages, self.hq, self.group_qids, self.group_size,
+                                  self.union_off, self.union_qmask, stream)
         else:
             pw_union_tables(self.bits, self.n_pages, self.group_rows, None, self.k,
                             self.union_off, self.union_pages, None, stream)

@@ -132,6 +132,27 @@ pw_status pw_group(const uint64_t* bits, int nq, int hkv, int n_pages, int windo
                           group_size, stream);
 }
 
+pw_status pw_arrange_groups(const uint64_t* bits, int nq, int hkv, int n_pages, int hq,
+                            int n_groups, int max_group, int32_t* group_qids,
+                            const int32_t* group_size, const int32_t* union_off,
+                            uint8_t* union_qmask, int64_t capacity, hipStream_t stream) {
+  pw::g_err[0] = 0;
+  if (nq < 0 || hkv < 1 || hq < 1 || n_pages < 1 || n_groups < 0 || capacity < 0)
+    return fail(PW_ERR_ARG, "pw_arrange_groups: bad sizes nq=%d hkv=%d hq=%d n_pages=%d n_groups=%d",
+                nq, hkv, hq, n_pages, n_groups);
+  if (hq % hkv) return fail(PW_ERR_ARG, "pw_arrange_groups: hq=%d not a multiple of hkv=%d", hq, hkv);
+  if (max_group < 1 || max_group > 8)
+    return fail(PW_ERR_UNSUPPORTED, "pw_arrange_groups: max_group=%d not in 1..8", max_group);
+  if (n_pages > 65536) return fail(PW_ERR_UNSUPPORTED, "pw_arrange_groups: n_pages=%d > 65536", n_pages);
+  // row tiles hold 16 query-head rows: only 4-member tiles (hq/hkv = 4) with groups of more
+  // than one tile have a choice to make
+  if (hq / hkv != 4 || max_group <= 4 || nq == 0 || n_groups == 0) return PW_OK;
+  if (!bits || !group_qids || !group_size || !union_off)
+    return fail(PW_ERR_ARG, "pw_arrange_groups: null required pointer");
+  return pw::launch_arrange(bits, nq, hkv, n_pages, n_groups, max_group, group_qids, group_size,
+                            union_off, union_qmask, capacity, stream);
+}
+
 pw_status pw_union_tables(const uint64_t* bits, int n_rows, int hkv, int n_pages,
                           const int32_t* group_rows, const int32_t* group_size, int n_groups,
                           int group_width, int k_max, int32_t* union_off, int32_t* union_pages,

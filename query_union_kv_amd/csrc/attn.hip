@@ -473,12 +473,16 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
         for (int dt = 0; dt < C::kDt; ++dt) o[m][dt] *= alpha;
         m_ref[m] = m_new;
-        const float bias = (sel && m_new != -INFINITY) ? lvs - m_new : -INFINITY;
-        lsum = 0.f;
+        // only the rows that moved their reference recompute P: every other row keeps its
+        // fast-path values, so a row's arithmetic never depends on its tile-mates
+        if (need) {
+          const float bias = (sel && m_new != -INFINITY) ? lvs - m_new : -INFINITY;
+          lsum = 0.f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          pv[k] = __builtin_amdgcn_exp2f(raw[k] + bias);
-          lsum += pv[k];
+          for (int k = 0; k < 8; ++k) {
+            pv[k] = __builtin_amdgcn_exp2f(raw[k] + bias);
+            lsum += pv[k];
+          }
         }
       }
 #pragma unroll

@@ -41,6 +41,12 @@ pw_status launch_prepare(const int32_t* topk, int nq, int hkv, int k, int n_page
                          int32_t* union_pages, uint8_t* union_qmask, int64_t capacity,
                          hipStream_t stream);
 
+// Member order of 5..8-member groups for 4-member row tiles, with member-mask bits to match.
+pw_status launch_arrange(const uint64_t* bits, int nq, int hkv, int n_pages, int n_groups,
+                         int max_group, int32_t* group_qids, const int32_t* group_size,
+                         const int32_t* union_off, uint8_t* union_qmask, int64_t capacity,
+                         hipStream_t stream);
+
 // Exclusive prefix sum in place: off[1..n] hold counts; afterwards off[i] = sum of the
 // first i counts (off[0] = 0).  One workgroup.
 pw_status launch_scan(int32_t* off, int n, hipStream_t stream);

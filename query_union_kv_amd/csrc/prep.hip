@@ -419,6 +419,105 @@ __global__ __launch_bounds__(256) void k_prepare(const int32_t* __restrict__ top
 }
 
 // ---------------------------------------------------------------------------------------
+// (2b) members arranged for row tiles (QUILT's cascaded sharing at row-tile granularity).
+// One wave per group of 5..8 members (4 members per 16-row tile).  A split is the three
+// positions {a < b < c} in 1..n-1 that join position 0 in the first tile; its cost is
+// |union of tile 1| + |union of tile 2|.  Lanes hold 64 bitset words of all members at a
+// time and every split's cost is summed over them.  The cheapest split, first in
+// lexicographic order on ties, orders the members (each tile keeps their relative order),
+// and the group's member-mask bits are permuted to match: new bit j = old bit order[j].
+__global__ __launch_bounds__(256) void k_arrange(const uint64_t* __restrict__ bits, int nq, int words,
+                                                 int n_tables, int n_groups, int max_group,
+                                                 int32_t* __restrict__ group_qids,
+                                                 const int32_t* __restrict__ group_size,
+                                                 const int32_t* __restrict__ union_off,
+                                                 uint8_t* __restrict__ union_qmask,
+                                                 int64_t capacity) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int e = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (e >= n_tables) return;
+  const int g = e / n_groups;
+  const int n = min(max(group_size[e], 0), max_group);
+  if (n <= 4 || n > 8) return;
+  int32_t* qids = group_qids + (int64_t)e * max_group;
+  int mem[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mem[i] = i < n ? qids[i] : 0;
+  // lanes hold 64 of the bitset words at a time; every split's cost is summed over the
+  // lanes.  Splits are indexed by their rank among all 35 triples of 1..7 in lexicographic
+  // order (a static index, so costs stay in registers); those with c > n-1 do not exist.
+  const int m = n - 1;
+  int costs[35];
+#pragma unroll
+  for (int i = 0; i < 35; ++i) costs[i] = 0;
+  for (int w0 = 0; w0 < words; w0 += kWave) {
+    const int w = w0 + lane;
+    uint64_t x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      x[i] = (i < n && w < words) ? bits[((int64_t)g * nq + mem[i]) * words + w] : 0ull;
+    int r = 0;
+#pragma unroll
+    for (int a = 1; a <= 7; ++a)
+#pragma unroll
+      for (int b = a + 1; b <= 7; ++b)
+#pragma unroll
+        for (int c = b + 1; c <= 7; ++c, ++r) {
+          if (c > m) continue;
+          const int mask = 1 | (1 << a) | (1 << b) | (1 << c);
+          uint64_t ua = 0, ub = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            if ((mask >> i) & 1) ua |= x[i];
+            else ub |= x[i];              // positions >= n hold zeros
+          }
+          costs[r] += wave_sum(__popcll(ua) + __popcll(ub));
+        }
+  }
+  int best_cost = 0x7fffffff, bmask = 0;
+  {
+    int r = 0;
+#pragma unroll
+    for (int a = 1; a <= 7; ++a)
+#pragma unroll
+      for (int b = a + 1; b <= 7; ++b)
+#pragma unroll
+        for (int c = b + 1; c <= 7; ++c, ++r)
+          if (c <= m && costs[r] < best_cost) {
+            best_cost = costs[r];
+            bmask = 1 | (1 << a) | (1 << b) | (1 << c);
+          }
+  }
+  // new position j holds old position order(j) = (perm >> 4j) & 15: the first tile's
+  // positions ascending, then the rest ascending
+  uint32_t perm = 0;
+  int k = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i < n && ((bmask >> i) & 1)) { perm |= (uint32_t)i << (4 * k); ++k; }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i < n && !((bmask >> i) & 1)) { perm |= (uint32_t)i << (4 * k); ++k; }
+  const int src = lane < 8 ? (int)((perm >> (4 * lane)) & 15u) : 0;
+  int newq = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) if (i == src) newq = mem[i];
+  if (lane < n) qids[lane] = newq;
+  if (union_qmask) {
+    const int64_t b0 = min<int64_t>(max(union_off[e], 0), capacity);
+    const int64_t b1 = min<int64_t>(union_off[e + 1], capacity);
+    for (int64_t x = b0 + lane; x < b1; x += kWave) {
+      const uint32_t old = union_qmask[x];
+      uint32_t nw = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < n) nw |= ((old >> ((perm >> (4 * j)) & 15u)) & 1u) << j;
+      union_qmask[x] = (uint8_t)nw;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // (3) union tables.  Table e = g * n_groups + j; one wave per table.
 __device__ __forceinline__ int member_count(const int32_t* group_size, int e, int group_width) {
   return group_size ? min(max(group_size[e], 0), group_width) : group_width;
@@ -536,6 +635,18 @@ __global__ void k_union_emit(const uint64_t* __restrict__ bits, int n_rows, int 
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
+pw_status launch_arrange(const uint64_t* bits, int nq, int hkv, int n_pages, int n_groups,
+                         int max_group, int32_t* group_qids, const int32_t* group_size,
+                         const int32_t* union_off, uint8_t* union_qmask, int64_t capacity,
+                         hipStream_t stream) {
+  const int n_tables = hkv * n_groups;
+  if (n_tables == 0) return PW_OK;
+  hipLaunchKernelGGL(k_arrange, dim3((n_tables + 3) / 4), dim3(256), 0, stream, bits, nq,
+                     (n_pages + 63) / 64, n_tables, n_groups, max_group, group_qids, group_size,
+                     union_off, union_qmask, capacity);
+  return check_launch("pw_arrange_groups");
+}
+
 pw_status launch_scan(int32_t* off, int n, hipStream_t stream) {
   hipLaunchKernelGGL(k_union_scan, dim3(1), dim3(1024), 0, stream, off, n);
   return check_launch("prefix sum");

@@ -30,7 +30,7 @@ def device_inputs(w, dev="cuda"):
     return d
 
 
-def make_plan(w, grouping="affinity", window=None, max_group=None, dev="cuda", fused=True):
+def make_plan(w, grouping="affinity", window=None, max_group=None, dev="cuda", fused=True, arrange=False):
     c = w.cfg
     ids = w.topk if w.topk is not None else w.mask_rows
     mode = "topk" if w.topk is not None else "block_union"
@@ -40,12 +40,13 @@ def make_plan(w, grouping="affinity", window=None, max_group=None, dev="cuda", f
                             kv_len=c.kv_len, k=ids.shape[2], window=window or c.window,
                             max_group=max_group or c.max_group, mode=mode, grouping=grouping,
                             n_rows=ids.shape[0] if mode == "block_union" else 0, fused=fused,
-                            device=dev)
+                            arrange=arrange, device=dev)
 
 
-def run_gpu(w, grouping="affinity", window=None, max_group=None, with_lse=True, fused=True):
+def run_gpu(w, grouping="affinity", window=None, max_group=None, with_lse=True, fused=True,
+            arrange=False):
     d = device_inputs(w)
-    plan = make_plan(w, grouping, window, max_group, fused=fused)
+    plan = make_plan(w, grouping, window, max_group, fused=fused, arrange=arrange)
     out = torch.full_like(d["q"], float("nan"))
     lse = torch.full(d["q"].shape[:2], float("nan"), dtype=torch.float32, device="cuda") if with_lse else None
     plan(d["ids"], d["q"], d["k"], d["v"], d["q_pos"], out, d["k_scale"], d["v_scale"], lse)
@@ -63,8 +64,9 @@ def run_gpu(w, grouping="affinity", window=None, max_group=None, with_lse=True, 
     return res, plan
 
 
-def oracle_tables(w, grouping="affinity", window=None, max_group=None):
-    """Bitsets, groups and union tables exactly as the oracle defines them."""
+def oracle_tables(w, grouping="affinity", window=None, max_group=None, arrange=False):
+    """Bitsets, groups and union tables exactly as the oracle defines them (optionally with
+    the members of every group arranged for 4-member row tiles when hq/hkv = 4)."""
     c = w.cfg
     window = window or c.window
     max_group = max_group or c.max_group
@@ -74,6 +76,8 @@ def oracle_tables(w, grouping="affinity", window=None, max_group=None):
             groups = [prep.group_affinity(b, window, max_group) for b in bits]
         else:
             groups = [prep.group_original(c.nq, max_group) for _ in bits]
+        if arrange and c.g == 4:
+            groups = [[prep.arrange_for_tiles(b, m, 4) for m in grp] for b, grp in zip(bits, groups)]
         qids, size = prep.groups_to_arrays(groups, max_group)
         off, pages, qmask = prep.union_tables(bits, groups)
         return {"bits": prep.bits_to_words(bits, c.n_pages), "group_qids": qids, "group_size": size,

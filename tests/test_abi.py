@@ -240,3 +240,20 @@ def test_shared_table_validation(kw, code):
 
 def test_shared_table_nothing_to_do_is_ok():
     assert _shared(nq=0, po=16, pl=16)[0] == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    # bits, nq, hkv, n_pages, hq, n_groups, mg, qids, size, off, qmask, cap, stream
+    ((NULL, 64, 2, 16, 8, 8, 9, NULL, NULL, NULL, NULL, 0, NULL), -2),     # max_group 9
+    ((NULL, 64, 2, 16, 7, 8, 8, NULL, NULL, NULL, NULL, 0, NULL), -1),     # hq % hkv
+    ((NULL, 64, 2, 70000, 8, 8, 8, NULL, NULL, NULL, NULL, 0, NULL), -2),  # n_pages
+    ((NULL, 64, 2, 16, 8, 8, 8, NULL, NULL, NULL, NULL, 0, NULL), -1),     # null pointers (G = 4)
+])
+def test_arrange_validation(args, code):
+    st, msg = _err(L.pw_arrange_groups(*args))
+    assert st == code and msg.startswith("pw_arrange_groups"), msg
+
+
+def test_arrange_is_a_noop_where_tiles_leave_no_choice():
+    assert L.pw_arrange_groups(NULL, 64, 2, 16, 16, 8, 8, NULL, NULL, NULL, NULL, 0, NULL) == 0  # G = 8
+    assert L.pw_arrange_groups(NULL, 64, 2, 16, 8, 16, 4, NULL, NULL, NULL, NULL, 0, NULL) == 0  # 4 members

@@ -210,3 +210,23 @@ def test_one_call_convenience_matches_oracle():
     O, L = oracle_attention(w, ref["S"])
     check_close(out.float().cpu().numpy(), O, cfg.kv_dtype, "sparse_prefill")
     check_lse(aux["lse"].cpu().numpy(), L, "sparse_prefill")
+
+
+ARRANGE = [("c2_gqa_bf16", {}), ("c3_long_fp8", {}), ("c1_tiny", {}),
+           ("small", dict(nq=200, k=6, kv_len=2048, hq=8, hkv=2)),
+           ("small", dict(nq=77, k=5, kv_len=2048, hq=8, hkv=2, window=30, max_group=6)),
+           ("small", dict(nq=150, k=8, kv_len=2048, hq=16, hkv=2))]      # G = 8: no-op
+
+
+@pytest.mark.parametrize("name,kw", ARRANGE, ids=[f"{n}-{i}" for i, (n, _) in enumerate(ARRANGE)])
+def test_tile_arrangement(name, kw):
+    """pw_arrange_groups: groups and member masks bit for bit against the oracle's
+    arrangement, and the attention output identical, bit for bit, to the unarranged run."""
+    cfg = CONFIGS[name] if name != "small" else _small(**kw)
+    print(f"[parity] tile arrangement {name} {kw}", flush=True)
+    w = make_workload(cfg)
+    res, _ = run_gpu(w, arrange=True)
+    ref = oracle_tables(w, arrange=True)
+    _compare_tables(res, ref)
+    base, _ = run_gpu(w)
+    assert np.array_equal(res["out"], base["out"]) and np.array_equal(res["lse"], base["lse"])
