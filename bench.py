@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--cpu-queries", type=int, default=4096,
                     help="oracle sample: the first N queries (whole windows), all KV heads")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--windows", default="256,512",
+                    help="extra grouping windows measured beside the configured one (TopK workloads)")
     ap.add_argument("--no-chunked", action="store_true",
                     help="skip the chunked-prefill leg (whole context in chunks of nq, overlap vs serial)")
     ap.add_argument("--profile-steps", type=int, default=None,
@@ -286,6 +288,24 @@ def main():
                              "execution_saving": t_orig_attn - t_fixed,
                              "online_cost": t_online - t_fixed, "net_saving": t_orig - t_online}
         exec_rows_pages = float((sizes * gsz).sum()) * cfg.g     # (row, union page) pairs
+
+        # Grouping window sweep: a wider bounded search finds more same-community queries
+        # (fewer page visits) but costs more preparation.
+        sweep = {}
+        for wn in [int(x) for x in args.windows.split(",") if x.strip()]:
+            if wn == cfg.window or wn % cfg.max_group:
+                continue
+            pw_plan = pw.SparsePrefill(nq=cfg.nq, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, n_pages=cfg.n_pages,
+                                       page_size=cfg.ps, kv_len=cfg.kv_len, k=ids.shape[2], window=wn,
+                                       max_group=cfg.max_group, device=dev)
+            t_p = timed(lambda: pw_plan.prepare(ids, stream))
+            t_a = timed(lambda: pw_plan.attend(q, kc, vc, q_pos, out, ks, vs, stream=stream))
+            sweep[str(wn)] = {"visits_per_query_kvh": int(pw_plan.union_off[-1].item()) / per_q,
+                              "prep_ms": t_p, "attn_ms": t_a}
+            del pw_plan
+        sweep[str(cfg.window)] = {"visits_per_query_kvh": total_pages / per_q,
+                                  "prep_ms": statistics.mean(t_prep), "attn_ms": t_fixed}
+        extras["window_sweep"] = sweep
 
         # Members arranged for 4-member row tiles (QUILT's cascaded sharing at row-tile
         # granularity): row tiles computed, from the member masks, and attention time.
