@@ -157,10 +157,17 @@ struct Cfg {
   static_assert(kTensorBytes % (16 * kThreads) == 0, "tile must split evenly into DMA slots");
   static_assert(kDmaPerTile * (ST - 2) < 64, "vmcnt range");
   static_assert(ST >= 2 && ST <= 4, "2..4 stages");
+  // Waves per SIMD the tile ring's LDS admits (160 KiB per CU, 4 SIMDs).  Where it admits
+  // three, the kernel is built for three (<= 168 VGPRs) and streams its K fragments
+  // instead of holding a whole tile's; elsewhere two waves with the K tile held in
+  // registers are faster.
+  static constexpr int kLdsWaves = (160 * 1024 / (ST * kStageBytes)) * NW / 4;
+  static constexpr int kWavesPerSimd = kLdsWaves >= 3 ? 3 : 2;
+  static constexpr bool kStreamK = kWavesPerSimd == 3;
 };
 
 template <int D, bool FP8, int MT, int NW, int ST>
-__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2))) void k_attn(Params p) {
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<D, FP8, MT, NW, ST>::kWavesPerSimd))) void k_attn(Params p) {
   using C = Cfg<D, FP8, MT, NW, ST>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[ST * C::kStageBytes];
 
@@ -199,23 +206,29 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   } else {
     gsize = min(p.max_group, p.nq - j * p.max_group);
   }
-  int qid[MT], hh[MT], row_lim[MT], my_bit[MT], mt_members[MT], mt_lim[MT], slot[MT];
+  // query ID (-1: none), query head and partial slot of this lane's row in row tile m;
+  // computed again in the epilogue rather than kept live through the tile loop
+  auto row_info = [&](int m, int& id, int& hq_row, int& slot) {
+    const int row = 16 * (wave * MT + m) + li;
+    const int member = row / p.G;
+    hq_row = g * p.G + (row - member * p.G);
+    id = -1;
+    if (member < gsize) id = qids ? qids[member] : j * p.max_group + member;
+    if (id >= p.nq) id = -1;
+    slot = -1;
+    if (p.out_slot && id >= 0) {
+      slot = p.out_slot[(int64_t)item * p.max_group + member];
+      if (slot < 0) id = -1;
+    }
+  };
+  int row_lim[MT], my_bit[MT], mt_members[MT], mt_lim[MT];
   bf16x8 qf[MT][C::kDc];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int row0 = 16 * (wave * MT + m);
-    const int row = row0 + li;
-    const int member = row / p.G;
-    hh[m] = g * p.G + (row - member * p.G);
-    int id = -1;
-    if (member < gsize) id = qids ? qids[member] : j * p.max_group + member;
-    if (id >= p.nq) id = -1;
-    slot[m] = -1;
-    if (p.out_slot && id >= 0) {
-      slot[m] = p.out_slot[(int64_t)item * p.max_group + member];
-      if (slot[m] < 0) id = -1;
-    }
-    qid[m] = id;
+    const int member = (row0 + li) / p.G;
+    int id, hh, slot;
+    row_info(m, id, hh, slot);
     const int qpos = id >= 0 ? p.q_pos[id] : -1;
     row_lim[m] = min(qpos, p.kv_len - 1);          // last usable token of this row
     int mm = 0;
@@ -238,7 +251,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
     for (int c = 0; c < C::kDc; ++c) {
       if (id >= 0) {
-        const i32x4 v = *reinterpret_cast<const i32x4*>(p.q + ((int64_t)id * p.hq + hh[m]) * D +
+        const i32x4 v = *reinterpret_cast<const i32x4*>(p.q + ((int64_t)id * p.hq + hh) * D +
                                                          32 * c + 8 * lq);
         qf[m][c] = __builtin_bit_cast(bf16x8, v);
       } else {
@@ -347,7 +360,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     for (int dt = 0; dt < C::kDt; ++dt) o[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_ref[m] = -INFINITY;
     l_run[m] = 0.f;
-    int lim = qid[m] >= 0 ? row_lim[m] : 0x7fffffff;
+    int lim = my_bit[m] != 0 ? row_lim[m] : 0x7fffffff;   // my_bit != 0: the row has a query
 #pragma unroll
     for (int sh = 1; sh < 16; sh <<= 1) lim = min(lim, __shfl_xor(lim, sh, kWave));
     mt_min[m] = __builtin_amdgcn_readfirstlane(lim);
@@ -360,7 +373,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   for (int m = 0; m < MT; ++m) {
 #pragma unroll
     for (int c = 0; c < C::kDc; ++c) asm volatile("" ::"v"(__builtin_bit_cast(i32x4, qf[m][c])));
-    asm volatile("" ::"v"(row_lim[m]), "v"(qid[m]));
+    asm volatile("" ::"v"(row_lim[m]), "v"(my_bit[m]));
   }
 
   // ---- one tile: S^T = K Q^T, masked online softmax, O^T += V^T P^T --------------------
@@ -393,18 +406,51 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     const float inv_vs = FP8 ? __builtin_amdgcn_rcpf(vs) : 1.f;
     const PW_LDS uint8_t* st = lds_p + SS * C::kStageBytes;
 
-    // K fragments (A operand of S^T = K . Q^T), shared by every row tile
-    bf16x8 ka[2][C::kDc];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int c = 0; c < C::kDc; ++c) {
-        if constexpr (FP8) {
-          ka[kb][c] = fp8x8_to_bf16(*reinterpret_cast<const PW_LDS i32x2*>(st + k_off[kb][c]));
-        } else {
-          ka[kb][c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const PW_LDS i32x4*>(st + k_off[kb][c]));
-        }
+    // K fragments (A operand of S^T = K . Q^T), shared by every row tile.  Held form:
+    // the whole tile's fragments are read first, then each row tile's MFMAs run.
+    // Streamed form: each fragment is read, converted and fed to every active row
+    // tile's MFMAs, then dropped (same products, same accumulation order).
+    auto kfrag = [&](int kb, int c) -> bf16x8 {
+      if constexpr (FP8) {
+        return fp8x8_to_bf16(*reinterpret_cast<const PW_LDS i32x2*>(st + k_off[kb][c]));
+      } else {
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const PW_LDS i32x4*>(st + k_off[kb][c]));
       }
+    };
+    bf16x8 ka[C::kStreamK ? 1 : 2][C::kStreamK ? 1 : C::kDc];
+    f32x4 s2all[C::kStreamK ? MT : 1][2];
+    if constexpr (C::kStreamK) {
+      auto qk_tiles = [&](auto act_c) {
+        constexpr int ACT = decltype(act_c)::value;   // bit m: row tile m active
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) s2all[m][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int c = 0; c < C::kDc; ++c) {
+            const bf16x8 kf = kfrag(kb, c);
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+              if (((ACT >> m) & 1) != 0)
+                s2all[m][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[m][c], s2all[m][kb], 0, 0, 0);
+          }
+      };
+      static_assert(MT <= 2, "row tiles per wave");
+      if constexpr (MT == 1) {
+        qk_tiles(std::integral_constant<int, 1>{});
+      } else {
+        if (act[0] && act[1]) qk_tiles(std::integral_constant<int, 3>{});
+        else if (act[0]) qk_tiles(std::integral_constant<int, 1>{});
+        else qk_tiles(std::integral_constant<int, 2>{});
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c = 0; c < C::kDc; ++c) ka[kb][c] = kfrag(kb, c);
+    }
 
     bf16x8 pf[MT];
 #pragma unroll
@@ -414,10 +460,14 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
       f32x4 s2[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s2[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (C::kStreamK) {
+          s2[kb] = s2all[m][kb];
+        } else {
+          s2[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < C::kDc; ++c)
-          s2[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][c], qf[m][c], s2[kb], 0, 0, 0);
+          for (int c = 0; c < C::kDc; ++c)
+            s2[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][c], qf[m][c], s2[kb], 0, 0, 0);
+        }
       }
       // lane holds row li of tile m and tile keys 8*lq + 4*kb + ii
       const bool sel = (qm & my_bit[m]) != 0;
@@ -536,13 +586,15 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   }
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    if (qid[m] < 0) continue;
+    int id, hh, slot;
+    row_info(m, id, hh, slot);
+    if (id < 0) continue;
     const float inv = l_run[m] > 0.f ? 1.0f / l_run[m] : 0.f;
-    int64_t orow = (int64_t)qid[m] * p.hq + hh[m];
+    int64_t orow = (int64_t)id * p.hq + hh;
     if (p.out_slot)          // page-major partial slot
-      orow = (int64_t)slot[m] * p.G + (hh[m] - g * p.G);
+      orow = (int64_t)slot * p.G + (hh - g * p.G);
     else if (p.n_split > 1)  // table-slice partial: slot (q, g, slice)
-      orow = (((int64_t)qid[m] * p.hkv + g) * p.n_split + slice) * p.G + (hh[m] - g * p.G);
+      orow = (((int64_t)id * p.hkv + g) * p.n_split + slice) * p.G + (hh - g * p.G);
     uint16_t* dst = p.out + orow * D;
 #pragma unroll
     for (int dt = 0; dt < C::kDt; ++dt) {
