@@ -58,6 +58,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 #define PW_LDS __attribute__((address_space(3)))
 #define PW_CONST __attribute__((address_space(4)))
 
@@ -164,6 +165,8 @@ struct Cfg {
   static constexpr int kLdsWaves = (160 * 1024 / (ST * kStageBytes)) * NW / 4;
   static constexpr int kWavesPerSimd = kLdsWaves >= 3 ? 3 : 2;
   static constexpr bool kStreamK = kWavesPerSimd == 3;
+  // fp8 K with d = 128: S^T = K . Q^T on the fp8 MFMA (16x16x128), K straight from LDS
+  static constexpr bool kF8Mma = FP8 && D == 128;
 };
 
 template <int D, bool FP8, int MT, int NW, int ST>
@@ -222,7 +225,9 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     }
   };
   int row_lim[MT], my_bit[MT], mt_members[MT], mt_lim[MT];
-  bf16x8 qf[MT][C::kDc];
+  bf16x8 qf[C::kF8Mma ? 1 : MT][C::kDc];
+  i32x8 qh[C::kF8Mma ? MT : 1], ql[C::kF8Mma ? MT : 1];
+  float qs[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int row0 = 16 * (wave * MT + m);
@@ -247,15 +252,66 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) lim = max(lim, __shfl_xor(lim, o, kWave));
     mt_lim[m] = __builtin_amdgcn_readfirstlane(lim);      // same in every lane
-    // Q^T fragments (B operand of S^T = K . Q^T): row li, d = 32c + 8lq .. +8
+    qs[m] = 1.f;
+    if constexpr (C::kF8Mma) {
+      // Q^T fragments for the fp8 MFMA: the row is scaled by 2^e (its largest magnitude
+      // lands in [128, 256)) and split into hi = e4m3(q 2^e) and lo = e4m3(q 2^e - hi).
+      // hi + lo equals q 2^e exactly for every element above 2^-10 of the row maximum (a
+      // bf16 significand is 8 bits, an e4m3 one 4), and 2^-e is undone in the score
+      // scale.  Lane group lq holds d = 16lq .. +16 (bytes 0..15) and 64 + 16lq .. +16
+      // (bytes 16..31), the same slots as the K operand.
+      float x[32];
 #pragma unroll
-    for (int c = 0; c < C::kDc; ++c) {
-      if (id >= 0) {
-        const i32x4 v = *reinterpret_cast<const i32x4*>(p.q + ((int64_t)id * p.hq + hh) * D +
-                                                         32 * c + 8 * lq);
-        qf[m][c] = __builtin_bit_cast(bf16x8, v);
-      } else {
-        qf[m][c] = bf16x8{};
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          i32x4 v = i32x4{0, 0, 0, 0};
+          if (id >= 0)
+            v = *reinterpret_cast<const i32x4*>(p.q + ((int64_t)id * p.hq + hh) * D + 64 * h + 16 * lq + 8 * w);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            x[16 * h + 8 * w + 2 * k] = __builtin_bit_cast(float, (int)((uint32_t)v[k] << 16));
+            x[16 * h + 8 * w + 2 * k + 1] = __builtin_bit_cast(float, (int)((uint32_t)v[k] & 0xFFFF0000u));
+          }
+        }
+      float mx = 0.f;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) mx = fmaxf(mx, fabsf(x[k]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      int ex = 0;
+      if (mx > 0.f && mx <= 3.0e38f) (void)frexpf(mx, &ex);   // mx = f 2^ex, f in [0.5, 1)
+      const int e = mx > 0.f && mx <= 3.0e38f ? 8 - ex : 0;
+      qs[m] = __builtin_amdgcn_ldexpf(1.f, -e);
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        float y[4], r[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) y[k] = __builtin_amdgcn_ldexpf(x[4 * w + k], e);
+        int hw = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        hw = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], hw, true);
+        const auto d0 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+        const auto d1 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+        r[0] = y[0] - d0[0];
+        r[1] = y[1] - d0[1];
+        r[2] = y[2] - d1[0];
+        r[3] = y[3] - d1[1];
+        int lw = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+        lw = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], lw, true);
+        qh[m][w] = hw;
+        ql[m][w] = lw;
+      }
+    } else {
+      // Q^T fragments (B operand of S^T = K . Q^T): row li, d = 32c + 8lq .. +8
+#pragma unroll
+      for (int c = 0; c < C::kDc; ++c) {
+        if (id >= 0) {
+          const i32x4 v = *reinterpret_cast<const i32x4*>(p.q + ((int64_t)id * p.hq + hh) * D +
+                                                           32 * c + 8 * lq);
+          qf[m][c] = __builtin_bit_cast(bf16x8, v);
+        } else {
+          qf[m][c] = bf16x8{};
+        }
       }
     }
   }
@@ -298,14 +354,20 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
   const PW_LDS uint8_t* lds_p = (const PW_LDS uint8_t*)lds;
 
   // per-lane LDS read offsets inside one stage (the stage base is an immediate)
-  int k_off[2][C::kDc];
+  // (fp8 MFMA: two whole 16-byte chunks per key block, d = 16lq .. +16 and 64 + 16lq .. +16)
+  int k_off[2][C::kF8Mma ? 2 : C::kDc];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int key = 8 * (li >> 2) + 4 * kb + (li & 3);   // MFMA row li of key block kb
+    if constexpr (C::kF8Mma) {
 #pragma unroll
-    for (int c = 0; c < C::kDc; ++c) {
-      const int byte = (32 * c + 8 * lq) * C::kEsz;
-      k_off[kb][c] = key * C::kRowBytes + (((byte >> 4) ^ swz<C::kChunks>(key)) << 4) + (byte & 15);
+      for (int h = 0; h < 2; ++h) k_off[kb][h] = key * C::kRowBytes + (((lq + 4 * h) ^ swz<C::kChunks>(key)) << 4);
+    } else {
+#pragma unroll
+      for (int c = 0; c < C::kDc; ++c) {
+        const int byte = (32 * c + 8 * lq) * C::kEsz;
+        k_off[kb][c] = key * C::kRowBytes + (((byte >> 4) ^ swz<C::kChunks>(key)) << 4) + (byte & 15);
+      }
     }
   }
   constexpr int kVr = FP8 ? C::kDt : 2 * C::kDt;
@@ -371,8 +433,15 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
   // loads would also wait for the whole ring.
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
+    if constexpr (C::kF8Mma) {
+      // (dword by dword: the host pass checks the constraint against its own registers)
 #pragma unroll
-    for (int c = 0; c < C::kDc; ++c) asm volatile("" ::"v"(__builtin_bit_cast(i32x4, qf[m][c])));
+      for (int w = 0; w < 8; ++w) asm volatile("" ::"v"(qh[m][w]), "v"(ql[m][w]));
+      asm volatile("" ::"v"(qs[m]));
+    } else {
+#pragma unroll
+      for (int c = 0; c < C::kDc; ++c) asm volatile("" ::"v"(__builtin_bit_cast(i32x4, qf[m][c])));
+    }
     asm volatile("" ::"v"(row_lim[m]), "v"(my_bit[m]));
   }
 
@@ -409,7 +478,18 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     // K fragments (A operand of S^T = K . Q^T), shared by every row tile.  Held form:
     // the whole tile's fragments are read first, then each row tile's MFMAs run.
     // Streamed form: each fragment is read, converted and fed to every active row
-    // tile's MFMAs, then dropped (same products, same accumulation order).
+    // tile's MFMAs, then dropped (same products, same accumulation order).  With the fp8
+    // MFMA a key block's fragment is its 32 e4m3 bytes per lane, used as stored, and one
+    // key block costs two MFMAs per row tile (Q's hi and lo parts).
+    auto kfrag8 = [&](int kb) -> i32x8 {
+      const i32x4 a = *reinterpret_cast<const PW_LDS i32x4*>(st + k_off[kb][0]);
+      const i32x4 b = *reinterpret_cast<const PW_LDS i32x4*>(st + k_off[kb][C::kF8Mma ? 1 : 0]);
+      return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    };
+    auto qk8 = [&](const i32x8& kf, int m, f32x4 acc) -> f32x4 {
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qh[m], acc, 0, 0, 0, 0, 0, 0);
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, ql[m], acc, 0, 0, 0, 0, 0, 0);
+    };
     auto kfrag = [&](int kb, int c) -> bf16x8 {
       if constexpr (FP8) {
         return fp8x8_to_bf16(*reinterpret_cast<const PW_LDS i32x2*>(st + k_off[kb][c]));
@@ -417,7 +497,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
         return __builtin_bit_cast(bf16x8, *reinterpret_cast<const PW_LDS i32x4*>(st + k_off[kb][c]));
       }
     };
-    bf16x8 ka[C::kStreamK ? 1 : 2][C::kStreamK ? 1 : C::kDc];
+    bf16x8 ka[C::kStreamK || C::kF8Mma ? 1 : 2][C::kStreamK || C::kF8Mma ? 1 : C::kDc];
+    i32x8 ka8[C::kF8Mma && !C::kStreamK ? 2 : 1];
     f32x4 s2all[C::kStreamK ? MT : 1][2];
     if constexpr (C::kStreamK) {
       auto qk_tiles = [&](auto act_c) {
@@ -427,15 +508,23 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) s2all[m][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int c = 0; c < C::kDc; ++c) {
-            const bf16x8 kf = kfrag(kb, c);
+        for (int kb = 0; kb < 2; ++kb) {
+          if constexpr (C::kF8Mma) {
+            const i32x8 kf = kfrag8(kb);
 #pragma unroll
             for (int m = 0; m < MT; ++m)
-              if (((ACT >> m) & 1) != 0)
-                s2all[m][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[m][c], s2all[m][kb], 0, 0, 0);
+              if (((ACT >> m) & 1) != 0) s2all[m][kb] = qk8(kf, m, s2all[m][kb]);
+          } else {
+#pragma unroll
+            for (int c = 0; c < C::kDc; ++c) {
+              const bf16x8 kf = kfrag(kb, c);
+#pragma unroll
+              for (int m = 0; m < MT; ++m)
+                if (((ACT >> m) & 1) != 0)
+                  s2all[m][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[m][c], s2all[m][kb], 0, 0, 0);
+            }
           }
+        }
       };
       static_assert(MT <= 2, "row tiles per wave");
       if constexpr (MT == 1) {
@@ -445,6 +534,9 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
         else if (act[0]) qk_tiles(std::integral_constant<int, 1>{});
         else qk_tiles(std::integral_constant<int, 2>{});
       }
+    } else if constexpr (C::kF8Mma) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) ka8[kb] = kfrag8(kb);
     } else {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -462,6 +554,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       for (int kb = 0; kb < 2; ++kb) {
         if constexpr (C::kStreamK) {
           s2[kb] = s2all[m][kb];
+        } else if constexpr (C::kF8Mma) {
+          s2[kb] = qk8(ka8[kb], m, f32x4{0.f, 0.f, 0.f, 0.f});
         } else {
           s2[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -470,6 +564,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
         }
       }
       // lane holds row li of tile m and tile keys 8*lq + 4*kb + ii
+      const float scm = C::kF8Mma ? sc * qs[m] : sc;   // fp8 MFMA: undo the row's 2^e
       const bool sel = (qm & my_bit[m]) != 0;
       const bool row_any = sel && tok0 <= row_lim[m];
       const bool tile_full = tok0 + kTK - 1 <= mt_min[m];          // uniform
@@ -480,7 +575,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
-            float v = __builtin_fmaf(s2[kb][ii], sc, bias);
+            float v = __builtin_fmaf(s2[kb][ii], scm, bias);
             if constexpr (decltype(masked_c)::value)
               if (tok0 + 8 * lq + 4 * kb + ii > row_lim[m]) v = -INFINITY;
             x[4 * kb + ii] = v;

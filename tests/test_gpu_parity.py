@@ -230,3 +230,39 @@ def test_tile_arrangement(name, kw):
     _compare_tables(res, ref)
     base, _ = run_gpu(w)
     assert np.array_equal(res["out"], base["out"]) and np.array_equal(res["lse"], base["lse"])
+
+
+def _scale_rows_bf16(bits, factors):
+    """bf16 bit patterns scaled elementwise by powers of two (exact: no overflow or
+    subnormal results for the exponents used here)."""
+    x = (bits.astype(np.uint32) << 16).view(np.float32) * factors.astype(np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 2)])
+def test_fp8_query_dynamic_range(hq, hkv):
+    """fp8 KV: query rows of very different magnitudes and rows whose elements span a wide
+    range (zero rows, rows scaled by 2^-40 .. 2^2, elements scaled by up to 2^-20, one
+    dominant element) against the definition."""
+    cfg = _small(kv_dtype="fp8", hq=hq, hkv=hkv, nq=96, k=8, kv_len=2048, seed=77)
+    w = make_workload(cfg)
+    rng = np.random.default_rng(5)
+    nq, d = cfg.nq, cfg.d
+    f = np.ones((nq, hq, d), dtype=np.float64)
+    row_exp = rng.choice([-40, -12, -3, 0, 1, 2], size=(nq, hq))
+    f *= np.exp2(row_exp)[:, :, None]
+    wide = rng.random((nq, hq)) < 0.3                       # elements spread over 2^-20 .. 1
+    f[wide] *= np.exp2(-rng.integers(0, 21, size=(int(wide.sum()), d)))
+    q = _scale_rows_bf16(w.q, f)
+    q[rng.random((nq, hq)) < 0.05] = 0                      # zero rows
+    spike = rng.random((nq, hq)) < 0.05                     # one dominant element
+    q[spike] = _scale_rows_bf16(q[spike], np.full((int(spike.sum()), d), 2.0 ** -16))
+    q[spike, 0] = 0x4100                                    # bf16 8.0
+    w.q = q
+    res, _ = run_gpu(w)
+    ref = oracle_tables(w)
+    _compare_tables(res, ref)
+    O, L = oracle_attention(w, ref["S"])
+    mx, mean, _ = check_close(res["out"], O, "fp8", f"dynamic range hq={hq}")
+    check_lse(res["lse"], L, f"dynamic range hq={hq}")
+    print(f"[parity] fp8 dynamic range hq={hq}: max_abs={mx:.3e} mean_abs={mean:.3e}", flush=True)
