@@ -220,6 +220,10 @@ pw_status pw_prepare(const int32_t* topk, int nq, int hkv, int k, int n_pages, i
  * union_off / union_pages / union_qmask: tables as written by pw_union_tables
  *             (union_qmask NULL = every member uses every page of its table)
  * capacity    entries in union_pages (reads are clamped to it)
+ * item_order  int32 [hkv*n_groups] or NULL: the order the work items are started in,
+ *             position r running item item_order[r] (see pw_schedule_items); must be a
+ *             permutation of 0 .. hkv*n_groups-1 (entries out of range are skipped).  It
+ *             changes no output bit.  Requires shared_table = 0.
  * out         bf16 [nq][hq][d]; each row written exactly once if it belongs to
  *             a group; rows of queries in no group are left untouched
  * lse         fp32 [nq][hq] or NULL
@@ -236,7 +240,22 @@ pw_status pw_sparse_prefill(const void* q, int nq, int hq, int hkv, int d,
                             const int32_t* group_qids, const int32_t* group_size, int n_groups,
                             int max_group, int shared_table, const int32_t* union_off,
                             const int32_t* union_pages, const uint8_t* union_qmask,
-                            int64_t capacity, void* out, float* lse, hipStream_t stream);
+                            int64_t capacity, const int32_t* item_order, void* out, float* lse,
+                            hipStream_t stream);
+
+/* ---- (4a) work order for (4) ---------------------------------------------------------------
+ * Not from the source pages: a scheduling aid for pw_sparse_prefill on this GPU.  Its
+ * work items run in 8 consecutive ranges of ceil(n_items / 8) positions, one range per
+ * XCD, started in position order; items differ in union size (the 64K fp8 Top16 workload:
+ * 61 .. 113 pages), and when the large ones come last they set the end of the launch.
+ * item_order lists every range's items by union size (union_off[e+1] - union_off[e]),
+ * largest first, ties by lower item index; a range longer than 8192 keeps item order.
+ *
+ * union_off   int32 [n_items + 1] (from pw_union_tables / pw_prepare)
+ * item_order  int32 [n_items] output, a permutation of 0 .. n_items-1
+ * Limits: n_items >= 0.                                                                     */
+pw_status pw_schedule_items(const int32_t* union_off, int n_items, int32_t* item_order,
+                            hipStream_t stream);
 
 /* ---- (4b) shared block tables with the table split across workgroups ---------------------
  * CompactAttention "Approach": with one block table per KV group (shared_table = 1 of

@@ -297,3 +297,23 @@ def tile_activations(bits_g: Sequence[int], groups: List[List[int]], tile_member
                 u |= bits_g[m]
             total += bin(u).count("1")
     return total
+
+
+# ---------------------------------------------------------------------------
+# work order of the union attention (not from the pages: a scheduling aid)
+
+
+def work_order(union_sizes: Sequence[int], ranges: int = 8, cap: int = 8192) -> List[int]:
+    """Start order of the attention's work items.  The n items are cut into `ranges`
+    consecutive ranges of ceil(n / ranges) positions; each range lists its own items by
+    union size, largest first, equal sizes by lower item index.  A range longer than
+    `cap` keeps item order.  Returns order[position] = item."""
+    n = len(union_sizes)
+    per = -(-n // ranges) if n else 0
+    order: List[int] = []
+    for r in range(ranges):
+        items = list(range(r * per, min(n, (r + 1) * per)))
+        if len(items) <= cap:
+            items.sort(key=lambda e: (-max(int(union_sizes[e]), 0), e))
+        order.extend(items)
+    return order

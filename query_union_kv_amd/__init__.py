@@ -23,6 +23,7 @@ import torch
 __all__ = [
     "PWError", "lib", "pw_version", "pw_words", "pw_num_groups", "pw_union_capacity",
     "pw_append_kv", "pw_page_bitsets", "pw_group", "pw_union_tables", "pw_prepare", "pw_sparse_prefill",
+    "pw_schedule_items",
     "SparsePrefill",
     "PW_KV_BF16", "PW_KV_FP8_E4M3", "LIB_PATH",
 ]
@@ -64,7 +65,8 @@ def lib() -> ctypes.CDLL:
             "pw_arrange_groups": (I, [P, I, I, I, I, I, I, P, P, P, P, I64, P]),
             "pw_prepare": (I, [P, I, I, I, I, I, I, P, P, P, P, P, P, P, I64, P]),
             "pw_sparse_prefill": (I, [P, I, I, I, I, P, P, I, P, P, I, I, I64, I64, P, I, F,
-                                      P, P, I, I, I, P, P, P, I64, P, P, P]),
+                                      P, P, I, I, I, P, P, P, I64, P, P, P, P]),
+            "pw_schedule_items": (I, [P, I, P, P]),
             "pw_shared_table_prefill": (I, [P, I, I, I, I, P, P, I, P, P, I, I, I64, I64, P, I, F,
                                             I, P, P, I64, I, P, P, P, P, P]),
             "pw_page_items_capacity": (I64, [I, I, I, I, I]),
@@ -256,8 +258,10 @@ def pw_sparse_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       union_qmask: Optional[torch.Tensor] = None,
                       k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
                       shared_table: bool = False, sm_scale: Optional[float] = None,
-                      lse: Optional[torch.Tensor] = None, stream=None) -> None:
-    """q bf16 [nq, hq, d]; k_cache/v_cache [hkv, n_pages, page_size, d] (bf16 or uint8 fp8 codes)."""
+                      lse: Optional[torch.Tensor] = None, item_order: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    """q bf16 [nq, hq, d]; k_cache/v_cache [hkv, n_pages, page_size, d] (bf16 or uint8 fp8 codes);
+    item_order: int32 [hkv * n_groups] work order from pw_schedule_items, or None."""
     nq, hq, d = q.shape
     if k_cache.shape != v_cache.shape or k_cache.dim() != 4 or k_cache.shape[0] != hkv:
         raise ValueError("k_cache/v_cache must be [hkv, n_pages, page_size, d]")
@@ -281,8 +285,18 @@ def pw_sparse_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _ptr(group_qids, torch.int32, "group_qids"), _ptr(group_size, torch.int32, "group_size"),
         n_groups, max_group, 1 if shared_table else 0, _ptr(union_off, torch.int32, "union_off"),
         _ptr(union_pages, torch.int32, "union_pages"), _ptr(union_qmask, torch.uint8, "union_qmask"),
-        union_pages.numel(), _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"),
-        _stream(stream)))
+        union_pages.numel(), _ptr(item_order, torch.int32, "item_order"),
+        _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
+def pw_schedule_items(union_off: torch.Tensor, item_order: torch.Tensor, stream=None) -> None:
+    """Work order for pw_sparse_prefill: each of the 8 consecutive position ranges lists its
+    items by union size, largest first (ties: lower item index)."""
+    n = union_off.numel() - 1
+    if item_order.numel() != n:
+        raise ValueError("item_order must hold one entry per table")
+    _check(lib().pw_schedule_items(_ptr(union_off, torch.int32, "union_off"), n,
+                                   _ptr(item_order, torch.int32, "item_order"), _stream(stream)))
 
 
 def _cache_dtype(k_cache: torch.Tensor) -> int:
@@ -464,6 +478,7 @@ class SparsePrefill:
     arrange: bool = False       # topk mode: members arranged for row tiles (pw_arrange_groups)
     n_split: int = 0            # block_union mode: table slices per KV head (0: enough to
                                 # give every SIMD two waves; 1: no partials)
+    schedule: bool = True       # topk mode: start the largest unions first (pw_schedule_items)
     device: str = "cuda"
 
     def __post_init__(self):
@@ -490,6 +505,7 @@ class SparsePrefill:
             self.group_qids = torch.empty((self.hkv, self.n_groups, self.max_group), **i32)
             self.group_size = torch.empty((self.hkv, self.n_groups), **i32)
             self.union_qmask = torch.empty(max(cap, 1), dtype=torch.uint8, device=dev)
+            self.item_order = torch.empty(n_tables, **i32) if self.schedule else None
             if self.grouping == "original":
                 ids = torch.arange(self.n_groups * self.max_group, **i32).view(self.n_groups, self.max_group)
                 ids = torch.where(ids < self.nq, ids, torch.full_like(ids, -1))
@@ -497,7 +513,7 @@ class SparsePrefill:
                 self.group_size.copy_((ids >= 0).sum(1, dtype=torch.int32).expand(self.hkv, -1))
         else:
             self.group_rows = torch.arange(self.n_rows, **i32).view(1, 1, -1).repeat(self.hkv, 1, 1)
-            self.group_qids = self.group_size = self.union_qmask = None
+            self.group_qids = self.group_size = self.union_qmask = self.item_order = None
             if self.n_split <= 0:
                 G = self.hq // self.hkv
                 waves = self.hkv * self.n_groups * max(1, -(-self.max_group * G // 32))
@@ -517,6 +533,8 @@ class SparsePrefill:
             if self.arrange:
                 pw_arrange_groups(self.bits, self.n_pages, self.hq, self.group_qids, self.group_size,
                                   self.union_off, self.union_qmask, stream)
+            if self.item_order is not None:
+                pw_schedule_items(self.union_off, self.item_order, stream)
             return
         pw_page_bitsets(ids, self.n_pages, self.bits, self.bad_ids, stream)
         if self.mode == "topk":
@@ -528,6 +546,8 @@ class SparsePrefill:
             if self.arrange:
                 pw_arrange_groups(self.bits, self.n_pages, self.hq, self.group_qids, self.group_size,
                                   self.union_off, self.union_qmask, stream)
+            if self.item_order is not None:
+                pw_schedule_items(self.union_off, self.item_order, stream)
         else:
             pw_union_tables(self.bits, self.n_pages, self.group_rows, None, self.k,
                             self.union_off, self.union_pages, None, stream)
@@ -547,7 +567,7 @@ class SparsePrefill:
                           group_qids=self.group_qids, group_size=self.group_size,
                           union_qmask=self.union_qmask, k_scale=k_scale, v_scale=v_scale,
                           shared_table=self.mode == "block_union", sm_scale=sm_scale, lse=lse,
-                          stream=stream)
+                          item_order=self.item_order, stream=stream)
 
     def __call__(self, ids, q, k_cache, v_cache, q_pos, out, k_scale=None, v_scale=None, lse=None,
                  stream=None) -> None:

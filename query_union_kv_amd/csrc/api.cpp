@@ -416,7 +416,7 @@ pw_status pw_shared_table_prefill(const void* q, int nq, int hq, int hkv, int d,
     return pw_sparse_prefill(q, nq, hq, hkv, d, k_cache, v_cache, kv_dtype, k_scale, v_scale,
                              page_size, n_pages, stride_head, stride_page, q_pos, kv_len, sm_scale,
                              nullptr, nullptr, n_groups, max_group, 1, union_off, union_pages,
-                             nullptr, capacity, out, lse, stream);
+                             nullptr, capacity, nullptr, out, lse, stream);
   if (hkv < 1 || hq < 1 || hq % hkv)
     return fail(PW_ERR_ARG, "pw_shared_table_prefill: hq=%d hkv=%d", hq, hkv);
   const int G = hq / hkv;
@@ -454,15 +454,28 @@ pw_status pw_sparse_prefill(const void* q, int nq, int hq, int hkv, int d, const
                             const int32_t* group_qids, const int32_t* group_size, int n_groups,
                             int max_group, int shared_table, const int32_t* union_off,
                             const int32_t* union_pages, const uint8_t* union_qmask,
-                            int64_t capacity, void* out, float* lse, hipStream_t stream) {
+                            int64_t capacity, const int32_t* item_order, void* out, float* lse,
+                            hipStream_t stream) {
   pw::g_err[0] = 0;
   pw::AttnArgs a{q, nq, hq, hkv, d, k_cache, v_cache, kv_dtype, k_scale, v_scale, page_size,
                  n_pages, stride_head, stride_page, q_pos, kv_len, sm_scale, group_qids, group_size,
                  n_groups, max_group, shared_table, union_off, union_pages, union_qmask, capacity,
                  out, lse};
+  a.item_order = item_order;
   const pw_status st = check_sparse_prefill(a, "pw_sparse_prefill");
   if (st != PW_OK || nq == 0 || n_groups == 0) return st;
+  if (item_order && shared_table)
+    return fail(PW_ERR_ARG, "pw_sparse_prefill: item_order needs shared_table = 0");
   return pw::launch_sparse_prefill(a, stream);
+}
+
+pw_status pw_schedule_items(const int32_t* union_off, int n_items, int32_t* item_order,
+                            hipStream_t stream) {
+  pw::g_err[0] = 0;
+  if (n_items < 0) return fail(PW_ERR_ARG, "pw_schedule_items: n_items=%d", n_items);
+  if (n_items == 0) return PW_OK;
+  if (!union_off || !item_order) return fail(PW_ERR_ARG, "pw_schedule_items: null pointer");
+  return pw::launch_schedule(union_off, n_items, item_order, stream);
 }
 
 }  // extern "C"

@@ -88,6 +88,7 @@ struct Params {
   int n_groups, max_group, shared_table;
   int n_split;             // > 1: each item's table is cut into n_split slices (partials)
   int n_items, items_per_xcd;
+  const int32_t* item_order;    // NULL or a permutation: position r runs item item_order[r]
   float score_scale;       // sm_scale * log2(e)
 };
 
@@ -175,8 +176,10 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
   __shared__ __attribute__((aligned(1024))) uint8_t lds[ST * C::kStageBytes];
 
   // XCD-aware work order: workgroup b runs on XCD b % 8; each XCD gets a contiguous
-  // range of items (KV-head-major), so one XCD's L2 serves neighbouring groups of the
-  // same KV head.
+  // range of positions (KV-head-major items), so one XCD's L2 serves neighbouring groups
+  // of the same KV head.  Workgroups are dispatched in order, so a work order that lists
+  // each range's largest unions first (pw_schedule_items) leaves the short items for the
+  // end, where they fill the gaps instead of extending the tail.
   const int b = blockIdx.x;
   int n_items = p.n_items, per_xcd = p.items_per_xcd, item0 = 0;
   if (p.item_lo_dev) {   // page-major: the grid is an upper bound of the device count
@@ -187,7 +190,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
   }
   const int item_rel = (b & 7) * per_xcd + (b >> 3);
   if (item_rel >= n_items) return;
-  const int item_s = item0 + item_rel;
+  const int item_s = p.item_order ? p.item_order[item_rel] : item0 + item_rel;
+  if (item_s < 0 || item_s >= item0 + n_items) return;   // (a damaged work order)
   // table slices: item_s = item * n_split + slice (consecutive slices share an XCD's L2)
   const int slice = p.n_split > 1 ? item_s % p.n_split : 0;
   const int item = p.n_split > 1 ? item_s / p.n_split : item_s;
@@ -768,6 +772,7 @@ pw_status launch_sparse_prefill(const AttnArgs& a, hipStream_t stream) {
   p.item_lo_dev = a.item_lo_dev;
   p.item_hi_dev = a.item_hi_dev;
   p.out_slot = a.out_slot;
+  p.item_order = a.n_split == 1 && !a.item_kvh ? a.item_order : nullptr;
   const int esz = a.kv_dtype == PW_KV_FP8_E4M3 ? 1 : 2;
   p.stride_head_b = a.stride_head * esz;
   p.stride_page_b = a.stride_page * esz;

@@ -50,6 +50,8 @@ pw_status launch_arrange(const uint64_t* bits, int nq, int hkv, int n_pages, int
 // Exclusive prefix sum in place: off[1..n] hold counts; afterwards off[i] = sum of the
 // first i counts (off[0] = 0).  One workgroup.
 pw_status launch_scan(int32_t* off, int n, hipStream_t stream);
+// Largest-first work order of n items (the work order of pw_schedule_items).
+pw_status launch_schedule(const int32_t* union_off, int n, int32_t* order, hipStream_t stream);
 
 // Page-major work items of the direct KV-page union, and the lse merge of its partials.
 size_t page_workspace_bytes(int nq, int hkv, int n_pages);
@@ -95,6 +97,9 @@ struct AttnArgs {
   const int32_t* item_lo_dev = nullptr;
   const int32_t* item_hi_dev = nullptr;
   const int32_t* out_slot = nullptr;
+  // Work order (NULL: item order): position r of the launch runs item item_order[r]
+  // (only with n_split == 1 and no page-major items).
+  const int32_t* item_order = nullptr;
 };
 
 pw_status launch_sparse_prefill(const AttnArgs& a, hipStream_t stream);

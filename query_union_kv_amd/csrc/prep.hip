@@ -579,6 +579,72 @@ __global__ void k_union_scan(int32_t* __restrict__ union_off, int n) {
   }
 }
 
+// Work order for the union attention: the n items are cut into 8 consecutive ranges of
+// per = ceil(n / 8) (the ranges the attention hands to the 8 XCDs) and each range is
+// listed by union size, largest first, ties by lower item index: the ascending order of
+// the keys (-size, index).  One workgroup per range runs a bitonic network.  Ranges of
+// up to 1024 items hold one 32-bit key per thread and exchange partners with lane
+// shuffles (distance < 64) or through LDS (distance >= 64); longer ranges, up to
+// kScheduleCap, sort 64-bit keys in LDS; a range longer than that keeps item order.
+constexpr int kScheduleCap = 8192;
+__global__ __launch_bounds__(1024) void k_schedule(const int32_t* __restrict__ union_off, int n,
+                                                   int per, int32_t* __restrict__ order) {
+  __shared__ uint64_t key[kScheduleCap];
+  const int lo = blockIdx.x * per;
+  const int m = min(n, lo + per) - lo;
+  if (m <= 0) return;
+  const int t = threadIdx.x;
+  if (m > kScheduleCap) {
+    for (int i = t; i < m; i += blockDim.x) order[lo + i] = lo + i;
+    return;
+  }
+  int N = 64;
+  while (N < m) N <<= 1;
+  auto size_of = [&](int i) { return max(union_off[lo + i + 1] - union_off[lo + i], 0); };
+  if (N <= 1024) {
+    // key = (2^19 - 1 - min(size, 2^19 - 1)) << 13 | local index; padding sorts last
+    uint32_t* k32 = reinterpret_cast<uint32_t*>(key);
+    uint32_t v = 0xFFFFFFFFu;
+    if (t < m) v = ((uint32_t)(0x7FFFF - min(size_of(t), 0x7FFFF)) << 13) | (uint32_t)t;
+    for (int k = 2; k <= N; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        uint32_t o;
+        if (j >= 64) {
+          if (t < N) k32[t] = v;
+          __syncthreads();
+          o = t < N ? k32[t ^ j] : v;
+          __syncthreads();
+        } else {
+          o = (uint32_t)__shfl_xor((int)v, j, 64);
+        }
+        const bool up = (t & k) == 0, lower = (t & j) == 0;
+        v = lower == up ? min(v, o) : max(v, o);
+      }
+    if (t < m) order[lo + t] = lo + (int)(v & 0x1FFFu);
+    return;
+  }
+  for (int i = t; i < N; i += blockDim.x) {
+    uint64_t k = ~0ull;   // padding sorts last
+    if (i < m) k = ((uint64_t)(uint32_t)(INT32_MAX - size_of(i)) << 32) | (uint32_t)(lo + i);
+    key[i] = k;
+  }
+  __syncthreads();
+  for (int k = 2; k <= N; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = t; i < N / 2; i += blockDim.x) {
+        const int a = ((i & ~(j - 1)) << 1) | (i & (j - 1));   // pair (a, a + j)
+        const bool up = (a & k) == 0;
+        const uint64_t ka = key[a], kb = key[a + j];
+        if ((ka > kb) == up) {
+          key[a] = kb;
+          key[a + j] = ka;
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = t; i < m; i += blockDim.x) order[lo + i] = (int32_t)(uint32_t)key[i];
+}
+
 template <bool QMASK>
 __global__ void k_union_emit(const uint64_t* __restrict__ bits, int n_rows, int words,
                              const int32_t* __restrict__ group_rows,
@@ -645,6 +711,15 @@ pw_status launch_arrange(const uint64_t* bits, int nq, int hkv, int n_pages, int
                      (n_pages + 63) / 64, n_tables, n_groups, max_group, group_qids, group_size,
                      union_off, union_qmask, capacity);
   return check_launch("pw_arrange_groups");
+}
+
+pw_status launch_schedule(const int32_t* union_off, int n, int32_t* order, hipStream_t stream) {
+  if (n <= 0) return PW_OK;
+  const int per = (n + 7) / 8;
+  int threads = 64;   // one thread per key up to 1024 keys per range
+  while (threads < per && threads < 1024) threads <<= 1;
+  hipLaunchKernelGGL(k_schedule, dim3(8), dim3(threads), 0, stream, union_off, n, per, order);
+  return check_launch("schedule_items");
 }
 
 pw_status launch_scan(int32_t* off, int n, hipStream_t stream) {

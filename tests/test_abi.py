@@ -94,7 +94,7 @@ def _attn(**kw):
     a = dict(q=NULL, nq=8, hq=4, hkv=1, d=128, k=NULL, v=NULL, kv_dtype=0, ks=NULL, vs=NULL, ps=64,
              n_pages=4, sh=4 * 64 * 128, sp=64 * 128, q_pos=NULL, kv_len=256, sm=0.088,
              gq=NULL, gs=NULL, n_groups=1, mg=8, shared=0, off=NULL, pages=NULL, qmask=NULL,
-             cap=4, out=NULL, lse=NULL, stream=NULL)
+             cap=4, order=NULL, out=NULL, lse=NULL, stream=NULL)
     a.update(kw)
     return _err(L.pw_sparse_prefill(*a.values()))
 
@@ -118,6 +118,20 @@ def test_attention_validation(kw, code):
 
 def test_attention_nothing_to_do_is_ok():
     assert _attn(nq=0)[0] == 0
+
+
+def test_work_order_needs_per_group_tables():
+    fake = 1 << 12      # aligned non-null stand-ins: rejected on the host before any launch
+    st, msg = _attn(q=fake, k=fake, v=fake, q_pos=fake, off=fake, pages=fake, out=fake, shared=1,
+                    order=fake)
+    assert st == -1 and "item_order" in msg, msg
+
+
+@pytest.mark.parametrize("n,off,order,code", [(-1, NULL, NULL, -1), (4, NULL, 4096, -1),
+                                              (4, 4096, NULL, -1), (0, NULL, NULL, 0)])
+def test_schedule_validation(n, off, order, code):
+    st, msg = _err(L.pw_schedule_items(off, n, order, NULL))
+    assert st == code and (code == 0 or msg.startswith("pw_schedule_items")), msg
     assert _attn(n_groups=0, nq=0)[0] == 0
 
 

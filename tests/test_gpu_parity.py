@@ -12,7 +12,10 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import (check_close, check_lse, oracle_attention, oracle_tables, run_gpu)
+import query_union_kv_amd as pw
+from gpu_util import (check_close, check_lse, device_inputs, oracle_attention, oracle_tables,
+                      run_gpu)
+from oracle import prep
 from helpers import add_padding_and_duplicates
 from workloads import CONFIGS, make_workload
 from workloads.configs import Config
@@ -196,7 +199,6 @@ def test_block_union_table_slices(n_split):
 
 
 def test_one_call_convenience_matches_oracle():
-    import query_union_kv_amd as pw
     from gpu_util import device_inputs
     cfg = _small(nq=130, k=8, kv_len=2048, hq=8, hkv=2, kv_dtype="fp8")
     w = make_workload(cfg)
@@ -266,3 +268,39 @@ def test_fp8_query_dynamic_range(hq, hkv):
     mx, mean, _ = check_close(res["out"], O, "fp8", f"dynamic range hq={hq}")
     check_lse(res["lse"], L, f"dynamic range hq={hq}")
     print(f"[parity] fp8 dynamic range hq={hq}: max_abs={mx:.3e} mean_abs={mean:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 100, 513, 4096, 8192, 8200, 65536, 65600])
+def test_work_order_matches_oracle(n):
+    """pw_schedule_items against the oracle's work order on synthetic union sizes: ranges
+    of <= 1024 items (one key per thread), longer ones (keys in LDS) and, at 65600 items,
+    ranges of 8200 > 8192 that keep item order."""
+    rng = np.random.default_rng(n)
+    sizes = rng.integers(0, 130, size=n).astype(np.int64)
+    sizes[rng.random(n) < 0.2] = 64                       # many ties
+    off = np.zeros(n + 1, dtype=np.int32)
+    off[1:] = np.cumsum(sizes)
+    order = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    pw.pw_schedule_items(torch.from_numpy(off).cuda(), order)
+    assert np.array_equal(order.cpu().numpy(), np.array(prep.work_order(sizes.tolist()), dtype=np.int32))
+
+
+@pytest.mark.parametrize("name", ["c2_gqa_bf16", "c3_long_fp8"])
+def test_work_order_changes_no_output_bit(name):
+    cfg = CONFIGS[name]
+    w = make_workload(cfg)
+    d = device_inputs(w)
+    outs = []
+    for schedule in (False, True):
+        plan = pw.SparsePrefill(nq=cfg.nq, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, n_pages=cfg.n_pages,
+                                page_size=cfg.ps, kv_len=cfg.kv_len, k=w.topk.shape[2],
+                                window=cfg.window, max_group=cfg.max_group, schedule=schedule)
+        out = torch.full_like(d["q"], float("nan"))
+        lse = torch.full(d["q"].shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+        plan(d["ids"], d["q"], d["k"], d["v"], d["q_pos"], out, d["k_scale"], d["v_scale"], lse)
+        torch.cuda.synchronize()
+        outs.append((out.view(torch.int16).cpu(), lse.cpu()))
+        if schedule:
+            sizes = np.diff(plan.union_off.cpu().numpy().astype(np.int64))
+            assert np.array_equal(plan.item_order.cpu().numpy(), np.array(prep.work_order(sizes.tolist())))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])

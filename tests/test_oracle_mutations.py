@@ -75,6 +75,12 @@ MUTATIONS = [
      lambda: K.test_scale_growth_reencodes_earlier_slots()),
     (kvcache, "_append_one", "if s_new > s_old:", "if s_new < s_old:",
      lambda: K.test_scale_kept_when_chunk_is_smaller()),
+    (prep, "work_order", "(-max(int(union_sizes[e]), 0), e)", "(max(int(union_sizes[e]), 0), e)",
+     lambda: P.test_work_order_hand_trace()),
+    (prep, "work_order", "(-max(int(union_sizes[e]), 0), e)", "(-max(int(union_sizes[e]), 0), -e)",
+     lambda: P.test_work_order_is_the_brute_force_order(0)),
+    (prep, "work_order", "per = -(-n // ranges) if n else 0", "per = n // ranges if n else 0",
+     lambda: P.test_work_order_hand_trace()),
 ]
 
 

@@ -5,6 +5,7 @@ the rest are hand traces, special cases, invariants, a brute-force optimality
 check of every greedy pick and set algebra written independently of the
 oracle's bit arithmetic.
 """
+import itertools
 import os
 import random
 
@@ -252,3 +253,35 @@ def test_arrange_for_tiles_is_the_brute_force_minimum():
             assert prep.tile_activations(bits, [arr], 4) == best
             # relative order kept inside each tile
             assert arr[:4] == sorted(arr[:4]) and arr[4:] == sorted(arr[4:])
+
+
+def test_work_order_hand_trace():
+    # ranges of ceil(9 / 3) = 3: sizes (3,5,5) -> 1,2,0; (1,9,2) -> 4,5,3; (2,7,4) -> 7,8,6
+    assert prep.work_order([3, 5, 5, 1, 9, 2, 2, 7, 4], ranges=3) == [1, 2, 0, 4, 5, 3, 7, 8, 6]
+    assert prep.work_order([4, 1, 7, 2, 2], ranges=8) == [0, 1, 2, 3, 4]      # one item per range
+    assert prep.work_order([1, 2, 3, 4], ranges=1, cap=3) == [0, 1, 2, 3]     # longer than cap
+    assert prep.work_order([], ranges=8) == []
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_work_order_is_the_brute_force_order(seed):
+    """Each range, by exhaustive search: the arrangement of its items whose size sequence is
+    non-increasing with equal sizes in increasing item order is unique and is the one."""
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 30))
+    ranges = int(rng.integers(1, 9))
+    sizes = [int(x) for x in rng.integers(0, 4, size=n)]
+    order = prep.work_order(sizes, ranges=ranges)
+    assert sorted(order) == list(range(n))
+    per = -(-n // ranges)
+    for r in range(ranges):
+        items = list(range(r * per, min(n, (r + 1) * per)))
+        if not items:
+            continue
+        got = order[r * per:r * per + len(items)]
+        if len(items) <= 6:
+            valid = [p for p in itertools.permutations(items)
+                     if all((sizes[a], -a) > (sizes[b], -b) for a, b in zip(p, p[1:]))]
+            assert valid == [tuple(got)]
+        assert sorted(got) == items
+        assert all(sizes[a] > sizes[b] or (sizes[a] == sizes[b] and a < b) for a, b in zip(got, got[1:]))
