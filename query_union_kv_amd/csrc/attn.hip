@@ -341,9 +341,6 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
   const uint8_t* vbase = p.v_cache + (int64_t)g * p.stride_head_b;
   // metadata through the scalar cache (constant address space): uniform per tile
   const PW_CONST int32_t* cpages = (const PW_CONST int32_t*)p.union_pages;
-  const PW_CONST uint8_t* cqmask = (const PW_CONST uint8_t*)p.union_qmask;
-  const PW_CONST float* cks = (const PW_CONST float*)p.k_scale;
-  const PW_CONST float* cvs = (const PW_CONST float*)p.v_scale;
 
   // per-lane byte offsets of this lane's DMA slots inside one K (or V) tile
   uint32_t dma_off[C::kDmaPerTensor];
@@ -400,12 +397,53 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     const int pg = cpages[e_begin + (t >> tpp_shift)];
     return (pg >= 0 && pg < p.n_pages) ? pg : -1;
   };
+
+  // Per-page metadata, one table entry per lane: entries md_base .. md_base + 63 of the
+  // item's table (relative to e_begin), refilled when the tile loop passes them (every
+  // 64 pages).  A tile reads its page's values with v_readlane instead of scalar loads:
+  // the K/V scales sit at random addresses, and their latency stalled every tile.
+  int md_base = 0, md_pq = 0;   // (page + 1) | member mask << 24 (page + 1 = 0: invalid)
+  float md_sc = 0.f, md_lvs = 0.f, md_ivs = 1.f;      // score scale * ks, log2 vs, 1 / vs
+  auto refill = [&](int base) {
+    md_base = base;
+    const int64_t e = e_begin + base + lane;
+    int pg = -1, qm = 0;
+    if (e < e_end) {
+      pg = p.union_pages[e];
+      pg = (pg >= 0 && pg < p.n_pages) ? pg : -1;
+      qm = p.union_qmask ? (int)p.union_qmask[e] : 0xFF;
+    }
+    md_pq = (pg + 1) | (qm << 24);   // n_pages <= 2^24 - 1
+    float ks = 1.f, vs = 1.f;
+    if constexpr (FP8) {
+      if (pg >= 0) {
+        ks = p.k_scale[(int64_t)g * p.n_pages + pg];
+        vs = p.v_scale[(int64_t)g * p.n_pages + pg];
+      }
+    }
+    md_sc = p.score_scale * ks;                        // log2-domain score scale
+    md_lvs = FP8 ? __builtin_amdgcn_logf(vs) : 0.f;    // log2 of the V page scale
+    // 1 / vs only scales the row sums, so the hardware reciprocal (1 ulp) is ample
+    md_ivs = FP8 ? __builtin_amdgcn_rcpf(vs) : 1.f;
+  };
+  auto lane_i = [](int v, int l) { return __builtin_amdgcn_readlane(v, l); };
+  auto lane_f = [](float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+  };
+
   // Every tile issues the same number of loads (an invalid page reads page 0 and is
   // never computed), so the vmcnt waits below are exact.
   auto issue = [&](int t, auto stage_c) {
     constexpr int SS = decltype(stage_c)::value;
-    const int pg = max(page_of(t), 0);
-    const int64_t off = (int64_t)pg * p.stride_page_b + (int64_t)(t & ((1 << tpp_shift) - 1)) * C::kTensorBytes;
+    const int ent = t >> tpp_shift;
+    int64_t pg_off;
+    if (ent - md_base < kWave) {   // held by the lanes (the loop never looks back)
+      const int pg = (lane_i(md_pq, ent - md_base) & 0xFFFFFF) - 1;
+      pg_off = (int64_t)__builtin_amdgcn_readfirstlane(max(pg, 0)) * p.stride_page_b;
+    } else {                       // a page past the held entries: the scalar table
+      pg_off = (int64_t)max(page_of(t), 0) * p.stride_page_b;
+    }
+    const int64_t off = pg_off + (int64_t)(t & ((1 << tpp_shift) - 1)) * C::kTensorBytes;
     const uint8_t* kt = kbase + off;
     const uint8_t* vt = vbase + off;
 #pragma unroll
@@ -432,6 +470,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     mt_min[m] = __builtin_amdgcn_readfirstlane(lim);
   }
 
+  refill(0);
+  asm volatile("" ::"v"(md_pq), "v"(md_sc), "v"(md_lvs), "v"(md_ivs));
   // Make every earlier global load complete here, before the first direct-to-LDS load is
   // issued: the compiler does not see those loads, so a wait it placed later for its own
   // loads would also wait for the whole ring.
@@ -452,14 +492,13 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
   // ---- one tile: S^T = K Q^T, masked online softmax, O^T += V^T P^T --------------------
   auto compute = [&](int t, auto stage_c) {
     constexpr int SS = decltype(stage_c)::value;
-    const int pg = page_of(t);
+    const int ent = t >> tpp_shift;
+    if (ent - md_base >= kWave) refill(ent & ~(kWave - 1));   // every 64 pages (uniform)
+    const int l = ent - md_base;
+    const int pq = lane_i(md_pq, l);
+    const int pg = (pq & 0xFFFFFF) - 1;
+    const int qm = (int)((uint32_t)pq >> 24);
     const int tok0 = pg * p.page_size + (t & ((1 << tpp_shift) - 1)) * kTK;
-    int qm = 0xFF;
-    if (cqmask) {   // member-mask byte, read through an aligned scalar dword load
-      const int64_t e = e_begin + (t >> tpp_shift);
-      const uint32_t w4 = ((const PW_CONST uint32_t*)cqmask)[e >> 2];
-      qm = (int)((w4 >> (8 * (int)(e & 3))) & 0xFF);
-    }
     bool act[MT];
     bool any = false;
 #pragma unroll
@@ -468,15 +507,9 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       any |= act[m];
     }
     if (!any) return;
-    float ks = 1.f, vs = 1.f;
-    if constexpr (FP8) {
-      ks = cks[(int64_t)g * p.n_pages + pg];
-      vs = cvs[(int64_t)g * p.n_pages + pg];
-    }
-    const float sc = p.score_scale * ks;                      // log2-domain score scale
-    const float lvs = FP8 ? __builtin_amdgcn_logf(vs) : 0.f;  // log2 of the V page scale
-    // 1 / vs only scales the row sums, so the hardware reciprocal (1 ulp) is ample
-    const float inv_vs = FP8 ? __builtin_amdgcn_rcpf(vs) : 1.f;
+    const float sc = lane_f(md_sc, l);
+    const float lvs = lane_f(md_lvs, l);
+    const float inv_vs = lane_f(md_ivs, l);
     const PW_LDS uint8_t* st = lds_p + SS * C::kStageBytes;
 
     // K fragments (A operand of S^T = K . Q^T), shared by every row tile.  Held form:
