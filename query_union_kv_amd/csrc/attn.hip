@@ -523,10 +523,6 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       const i32x4 b = *reinterpret_cast<const PW_LDS i32x4*>(st + k_off[kb][C::kF8Mma ? 1 : 0]);
       return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     };
-    auto qk8 = [&](const i32x8& kf, int m, f32x4 acc) -> f32x4 {
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qh[m], acc, 0, 0, 0, 0, 0, 0);
-      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, ql[m], acc, 0, 0, 0, 0, 0, 0);
-    };
     auto kfrag = [&](int kb, int c) -> bf16x8 {
       if constexpr (FP8) {
         return fp8x8_to_bf16(*reinterpret_cast<const PW_LDS i32x2*>(st + k_off[kb][c]));
@@ -546,11 +542,16 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
           for (int kb = 0; kb < 2; ++kb) s2all[m][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          if constexpr (C::kF8Mma) {
+          if constexpr (C::kF8Mma) {   // every hi product before the lo ones that depend on it
             const i32x8 kf = kfrag8(kb);
 #pragma unroll
             for (int m = 0; m < MT; ++m)
-              if (((ACT >> m) & 1) != 0) s2all[m][kb] = qk8(kf, m, s2all[m][kb]);
+              if (((ACT >> m) & 1) != 0)
+                s2all[m][kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qh[m], s2all[m][kb], 0, 0, 0, 0, 0, 0);
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+              if (((ACT >> m) & 1) != 0)
+                s2all[m][kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, ql[m], s2all[m][kb], 0, 0, 0, 0, 0, 0);
           } else {
 #pragma unroll
             for (int c = 0; c < C::kDc; ++c) {
@@ -587,13 +588,20 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       pf[m] = bf16x8{};
       if (!act[m]) continue;
       f32x4 s2[2];
+      if constexpr (C::kF8Mma && !C::kStreamK) {   // both key blocks' hi products, then lo
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          s2[kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka8[kb], qh[m], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                     0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          s2[kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka8[kb], ql[m], s2[kb], 0, 0, 0, 0, 0, 0);
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if constexpr (C::kStreamK) {
           s2[kb] = s2all[m][kb];
-        } else if constexpr (C::kF8Mma) {
-          s2[kb] = qk8(ka8[kb], m, f32x4{0.f, 0.f, 0.f, 0.f});
-        } else {
+        } else if constexpr (!C::kF8Mma) {   // (the held fp8 form computed S above)
           s2[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int c = 0; c < C::kDc; ++c)
@@ -608,13 +616,15 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       // scores in the log2 domain; keys after a row's last usable token -> -inf.  A tile
       // wholly before every row's limit (the common case) needs no causal compare.
       auto scores = [&](float bias, float* x, auto masked_c) {
+        // key tok0 + 8lq + 4kb + ii is past the row's limit iff 4kb + ii > rel
+        const int rel = decltype(masked_c)::value ? row_lim[m] - tok0 - 8 * lq : 0;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
             float v = __builtin_fmaf(s2[kb][ii], scm, bias);
             if constexpr (decltype(masked_c)::value)
-              if (tok0 + 8 * lq + 4 * kb + ii > row_lim[m]) v = -INFINITY;
+              if (4 * kb + ii > rel) v = -INFINITY;
             x[4 * kb + ii] = v;
           }
       };
@@ -637,7 +647,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       // row sum passed 2^30, or overflowed): rare, wave-uniform slow path.  The decision is
       // made per row - lanes li, li+16, li+32 and li+48 hold row li - so that every key of
       // a row is exponentiated against the same reference.
-      const bool need_lane = row_any && (m_ref[m] == -INFINITY || !(lsum * inv_vs <= 0x1p30f));
+      // (bitwise, not short-circuit: straight-line compares instead of exec-mask branches)
+      const bool need_lane = row_any & ((m_ref[m] == -INFINITY) | !(lsum * inv_vs <= 0x1p30f));
       const uint64_t nb = __builtin_amdgcn_ballot_w64(need_lane);
       if (nb) {
         const uint32_t rows = (uint32_t)(nb | (nb >> 16) | (nb >> 32) | (nb >> 48)) & 0xFFFFu;
