@@ -406,21 +406,35 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
   float md_sc = 0.f, md_lvs = 0.f, md_ivs = 1.f;      // score scale * ks, log2 vs, 1 / vs
   auto refill = [&](int base) {
     md_base = base;
-    const int64_t e = e_begin + base + lane;
     int pg = -1, qm = 0;
-    if (e < e_end) {
-      pg = p.union_pages[e];
-      pg = (pg >= 0 && pg < p.n_pages) ? pg : -1;
-      qm = p.union_qmask ? (int)p.union_qmask[e] : 0xFF;
-    }
-    md_pq = (pg + 1) | (qm << 24);   // n_pages <= 2^24 - 1
     float ks = 1.f, vs = 1.f;
-    if constexpr (FP8) {
-      if (pg >= 0) {
-        ks = p.k_scale[(int64_t)g * p.n_pages + pg];
-        vs = p.v_scale[(int64_t)g * p.n_pages + pg];
+    if (p.item_kvh) {
+      // page-major items hold one page: every lane takes it through the scalar cache,
+      // whose round trip is shorter than a vector load's on these two-tile items
+      pg = cpages[e_begin];
+      pg = (pg >= 0 && pg < p.n_pages) ? pg : -1;
+      qm = 0xFF;
+      if constexpr (FP8) {
+        if (pg >= 0) {
+          ks = ((const PW_CONST float*)p.k_scale)[(int64_t)g * p.n_pages + pg];
+          vs = ((const PW_CONST float*)p.v_scale)[(int64_t)g * p.n_pages + pg];
+        }
+      }
+    } else {
+      const int64_t e = e_begin + base + lane;
+      if (e < e_end) {
+        pg = p.union_pages[e];
+        pg = (pg >= 0 && pg < p.n_pages) ? pg : -1;
+        qm = p.union_qmask ? (int)p.union_qmask[e] : 0xFF;
+      }
+      if constexpr (FP8) {
+        if (pg >= 0) {
+          ks = p.k_scale[(int64_t)g * p.n_pages + pg];
+          vs = p.v_scale[(int64_t)g * p.n_pages + pg];
+        }
       }
     }
+    md_pq = (pg + 1) | (qm << 24);   // n_pages <= 2^24 - 1
     md_sc = p.score_scale * ks;                        // log2-domain score scale
     md_lvs = FP8 ? __builtin_amdgcn_logf(vs) : 0.f;    // log2 of the V page scale
     // 1 / vs only scales the row sums, so the hardware reciprocal (1 ulp) is ample
