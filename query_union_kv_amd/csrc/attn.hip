@@ -596,6 +596,26 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
         for (int c = 0; c < C::kDc; ++c) ka[kb][c] = kfrag(kb, c);
     }
 
+    // V^T fragments (A operand of O^T += V^T . P^T): lane li = d column 16*dt + li, k-slots
+    // e = tile keys 8*lq + e.  One-wave items read and convert them here, ahead of the
+    // softmax, so that the LDS latency and the conversions overlap the QK MFMAs; the
+    // three-wave forms (no registers to spare) read each right before its MFMAs.
+    constexpr bool kEarlyV = !C::kStreamK;
+    auto vfrag = [&](int dt) -> bf16x8 {
+      if constexpr (FP8) {
+        return fp8x8_to_bf16(__builtin_amdgcn_ds_read_tr8_b64_v2i32((PW_LDS i32x2*)(st + v_off[dt])));
+      } else {
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PW_LDS bf16x4*)(st + v_off[2 * dt]));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PW_LDS bf16x4*)(st + v_off[2 * dt + 1]));
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    };
+    bf16x8 va[kEarlyV ? C::kDt : 1];
+    if constexpr (kEarlyV) {
+#pragma unroll
+      for (int dt = 0; dt < C::kDt; ++dt) va[dt] = vfrag(dt);
+    }
+
     bf16x8 pf[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -697,18 +717,12 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       l_run[m] += lsum * inv_vs;
     }
 
-    // O^T[d][row] += V^T . P^T for every row tile (an unused tile has P = 0): A operand
-    // lane li = d column 16*dt + li, k-slots e = tile keys 8*lq + e
+    // O^T[d][row] += V^T . P^T for every row tile (an unused tile has P = 0)
 #pragma unroll
     for (int dt = 0; dt < C::kDt; ++dt) {
       bf16x8 a;
-      if constexpr (FP8) {
-        a = fp8x8_to_bf16(__builtin_amdgcn_ds_read_tr8_b64_v2i32((PW_LDS i32x2*)(st + v_off[dt])));
-      } else {
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PW_LDS bf16x4*)(st + v_off[2 * dt]));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PW_LDS bf16x4*)(st + v_off[2 * dt + 1]));
-        a = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
+      if constexpr (kEarlyV) a = va[dt];
+      else a = vfrag(dt);
 #pragma unroll
       for (int m = 0; m < MT; ++m)
         o[m][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[m], o[m][dt], 0, 0, 0);
