@@ -717,15 +717,25 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       l_run[m] += lsum * inv_vs;
     }
 
-    // O^T[d][row] += V^T . P^T for every row tile (an unused tile has P = 0)
+    // O^T[d][row] += V^T . P^T.  With the fragments already in registers, each row tile's
+    // MFMAs form one block behind one uniform branch, and an inactive row tile (P = 0)
+    // skips its block; otherwise every row tile runs (its P is 0 when inactive).
+    if constexpr (kEarlyV) {
 #pragma unroll
-    for (int dt = 0; dt < C::kDt; ++dt) {
-      bf16x8 a;
-      if constexpr (kEarlyV) a = va[dt];
-      else a = vfrag(dt);
+      for (int m = 0; m < MT; ++m) {
+        if (MT > 1 && !act[m]) continue;
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-        o[m][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[m], o[m][dt], 0, 0, 0);
+        for (int dt = 0; dt < C::kDt; ++dt)
+          o[m][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pf[m], o[m][dt], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < C::kDt; ++dt) {
+        const bf16x8 a = vfrag(dt);
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          o[m][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[m], o[m][dt], 0, 0, 0);
+      }
     }
   };
 
