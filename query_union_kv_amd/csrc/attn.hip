@@ -1,4 +1,5 @@
-// ID-aware union attention for gfx950 (CDNA4, wave64, MFMA 16x16x32 bf16).
+// ID-aware union attention for gfx950 (CDNA4, wave64; MFMA 16x16x32 bf16 and, for fp8 K,
+// 16x16x128 fp8).
 //
 // Method: "PageWeaver: KV-Guided Query Unions for Sparse Attention" (abstract,
 // Fig. 1, Fig. 3): a group's union pages are staged on chip once and the same
@@ -23,14 +24,16 @@
 //     the lane;
 //   * support mask (the member selected the page) + causal mask, online
 //     softmax in the log2 domain; the reference used for the exponentials
-//     is set on a row's first used tile and raised only when a tile's row
-//     sum of P = 2^(score - reference) passes 2^32, so the accumulators are
-//     rescaled rarely (exact either way: numerator and denominator share
-//     the reference);
+//     is set on a row's first used tile and raised only when a lane's share
+//     of a tile's row sum of P = 2^(score - reference) passes 2^30, so the
+//     accumulators are rescaled rarely (exact either way: numerator and
+//     denominator share the reference);
 //   * O^T[d][row] += V^T . P^T on MFMA, V^T read from LDS with the CDNA4
 //     transposing loads (ds_read_b64_tr_b8 / _b16).
-// fp8 (OCP e4m3fn) codes are converted exactly to bf16; the K page scale folds
-// into the score scale and the V page scale into P (the row sum uses unscaled P).
+// fp8 (OCP e4m3fn) K codes feed the fp8 MFMA as stored (d = 128: each Q row split
+// exactly into two e4m3 parts) or convert exactly to bf16 (d = 64); V codes convert
+// exactly to bf16.  The K page scale folds into the score scale and the V page scale
+// into P (the row sum uses unscaled P).
 #include <hip/hip_runtime.h>
 
 #include <stdlib.h>
@@ -47,10 +50,11 @@ constexpr int kWave = 64;
 constexpr int kTK = 32;               // tokens per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// The reference used for the exponentials is raised only when a tile's row sum of P
-// exceeds 2^kRescaleLog2 (P = 2^(score - reference)): well inside fp32/bf16 range, and
-// bf16/fp32 precision is relative, so nothing is lost while P stays below it.
-constexpr float kRescaleLog2 = 32.0f;
+// The reference used for the exponentials is raised only when a lane's share of a tile's
+// row sum of P (P = 2^(score - reference)) exceeds 2^30 (the tile's row sum then 2^32 at
+// most): well inside fp32/bf16 range, and bf16/fp32 precision is relative, so nothing is
+// lost while P stays below it.
+constexpr float kRescaleShare = 0x1p30f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -682,7 +686,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       // made per row - lanes li, li+16, li+32 and li+48 hold row li - so that every key of
       // a row is exponentiated against the same reference.
       // (bitwise, not short-circuit: straight-line compares instead of exec-mask branches)
-      const bool need_lane = row_any & ((m_ref[m] == -INFINITY) | !(lsum * inv_vs <= 0x1p30f));
+      const bool need_lane = row_any & ((m_ref[m] == -INFINITY) | !(lsum * inv_vs <= kRescaleShare));
       const uint64_t nb = __builtin_amdgcn_ballot_w64(need_lane);
       if (nb) {
         const uint32_t rows = (uint32_t)(nb | (nb >> 16) | (nb >> 32) | (nb >> 48)) & 0xFFFFu;
