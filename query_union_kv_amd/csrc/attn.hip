@@ -116,18 +116,45 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 v) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// Direct global -> LDS copy of 16 bytes per lane from sbase + voff (sbase wave-uniform,
-// voff per lane): lane l's bytes land at LDS address lds + 16*l.  M0 carries the LDS
-// address and is restored afterwards.
-__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
-  // M0 holds the LDS destination; it is declared clobbered, so the compiler restores
-  // whatever it keeps there itself
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(voff), "s"(sbase), "s"(lds)
-      : "memory", "m0");
+// Direct global -> LDS copies of 16 bytes per lane, N loads sharing one M0 (the LDS
+// address; declared clobbered, so the compiler restores whatever it keeps there).  Load k
+// reads sbase + voff[k] + k*STRIDE (sbase wave-uniform, voff per lane) and lands at LDS
+// m0 + k*STRIDE + 16*l for lane l: the instruction offset applies to both addresses
+// (measured).  The offset field holds < 4096.  The leading s_nop separates the M0 write
+// from a preceding load that reads M0.
+template <int N, int STRIDE>
+__device__ __forceinline__ void dma16_group(const uint32_t* voff, const void* sbase, uint32_t m0) {
+  static_assert((N == 1 || N == 2 || N == 4) && (N - 1) * STRIDE < 4096, "offset field");
+  if constexpr (N == 1) {
+    asm volatile(
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %0, %2"
+        :
+        : "v"(voff[0]), "s"(m0), "s"(sbase)
+        : "memory", "m0");
+  } else if constexpr (N == 2) {
+    asm volatile(
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %0, %3\n\t"
+        "global_load_lds_dwordx4 %1, %3 offset:%4"
+        :
+        : "v"(voff[0]), "v"(voff[1]), "s"(m0), "s"(sbase), "n"(STRIDE)
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %4\n\t"
+        "global_load_lds_dwordx4 %0, %5\n\t"
+        "global_load_lds_dwordx4 %1, %5 offset:%6\n\t"
+        "global_load_lds_dwordx4 %2, %5 offset:%7\n\t"
+        "global_load_lds_dwordx4 %3, %5 offset:%8"
+        :
+        : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(m0), "s"(sbase), "n"(STRIDE),
+          "n"(2 * STRIDE), "n"(3 * STRIDE)
+        : "memory", "m0");
+  }
 }
 
 template <int N>
@@ -158,6 +185,11 @@ struct Cfg {
   static constexpr int kDmaPerTensor = kTensorBytes / (16 * kThreads);  // per lane
   static_assert(kDmaPerTensor >= 1, "every wave issues at least one load per tensor");
   static constexpr int kDmaPerTile = 2 * kDmaPerTensor;
+  // a tensor's loads go out in groups of kDmaGroup sharing one M0: load k of a group sits
+  // k * NW KiB above the group's first in both memories, within the 4 KiB offset field
+  static constexpr int kDmaGroup = (kDmaPerTensor % 4 == 0 && 4 * NW <= 4)   ? 4
+                                   : (kDmaPerTensor % 2 == 0 && 2 * NW <= 4) ? 2
+                                                                             : 1;
   static constexpr int kDc = D / 32;                       // MFMA k-steps over d
   static constexpr int kDt = D / 16;                       // 16-wide d tiles of O
   static_assert(kTensorBytes % (16 * kThreads) == 0, "tile must split evenly into DMA slots");
@@ -353,7 +385,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     const int slot = (i * NW + wave) * kWave + lane;
     const int r = slot / C::kChunks;
     const int pc = slot - r * C::kChunks;
-    dma_off[i] = r * C::kRowBytes + ((pc ^ swz<C::kChunks>(r)) << 4);
+    // less the in-group offset that the load instruction adds back
+    dma_off[i] = r * C::kRowBytes + ((pc ^ swz<C::kChunks>(r)) << 4) - (i % C::kDmaGroup) * NW * 1024;
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(PW_LDS void*)lds;
   const PW_LDS uint8_t* lds_p = (const PW_LDS uint8_t*)lds;
@@ -464,12 +497,14 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     const int64_t off = pg_off + (int64_t)(t & ((1 << tpp_shift) - 1)) * C::kTensorBytes;
     const uint8_t* kt = kbase + off;
     const uint8_t* vt = vbase + off;
+    constexpr int GN = C::kDmaGroup;
 #pragma unroll
-    for (int i = 0; i < C::kDmaPerTensor; ++i)
-      dma16(dma_off[i], kt, lds_base + SS * C::kStageBytes + (i * NW + wave) * (kWave * 16));
+    for (int i = 0; i < C::kDmaPerTensor; i += GN)
+      dma16_group<GN, NW * 1024>(dma_off + i, kt, lds_base + SS * C::kStageBytes + (i * NW + wave) * (kWave * 16));
 #pragma unroll
-    for (int i = 0; i < C::kDmaPerTensor; ++i)
-      dma16(dma_off[i], vt, lds_base + SS * C::kStageBytes + C::kTensorBytes + (i * NW + wave) * (kWave * 16));
+    for (int i = 0; i < C::kDmaPerTensor; i += GN)
+      dma16_group<GN, NW * 1024>(dma_off + i, vt,
+                                 lds_base + SS * C::kStageBytes + C::kTensorBytes + (i * NW + wave) * (kWave * 16));
   };
 
   // ---- running state ------------------------------------------------------------------
