@@ -484,11 +484,15 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
 
   // Every tile issues the same number of loads (an invalid page reads page 0 and is
   // never computed), so the vmcnt waits below are exact.
-  auto issue = [&](int t, auto stage_c) {
+  // pg_known: the tile's page when the caller has it already (kNoPage: look it up)
+  constexpr int kNoPage = -2;
+  auto issue = [&](int t, auto stage_c, int pg_known) {
     constexpr int SS = decltype(stage_c)::value;
     const int ent = t >> tpp_shift;
     int64_t pg_off;
-    if (ent - md_base < kWave) {   // held by the lanes (the loop never looks back)
+    if (pg_known != kNoPage) {
+      pg_off = (int64_t)max(pg_known, 0) * p.stride_page_b;
+    } else if (ent - md_base < kWave) {   // held by the lanes (the loop never looks back)
       const int pg = (lane_i(md_pq, ent - md_base) & 0xFFFFFF) - 1;
       pg_off = (int64_t)__builtin_amdgcn_readfirstlane(max(pg, 0)) * p.stride_page_b;
     } else {                       // a page past the held entries: the scalar table
@@ -543,26 +547,44 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
   }
 
   // ---- one tile: S^T = K Q^T, masked online softmax, O^T += V^T P^T --------------------
-  auto compute = [&](int t, auto stage_c) {
-    constexpr int SS = decltype(stage_c)::value;
+  // what a tile needs of its page: shared by the tiles of one page
+  struct PageCtx {
+    int pg, qm, abits;        // page (-1: invalid), member mask, bit m: row tile m selects it
+    float sc, lvs, inv_vs;    // score scale * ks, log2 vs, 1 / vs
+  };
+  auto page_ctx = [&](int t) {
     const int ent = t >> tpp_shift;
     if (ent - md_base >= kWave) refill(ent & ~(kWave - 1));   // every 64 pages (uniform)
     const int l = ent - md_base;
     const int pq = lane_i(md_pq, l);
-    const int pg = (pq & 0xFFFFFF) - 1;
-    const int qm = (int)((uint32_t)pq >> 24);
+    PageCtx c;
+    c.pg = (pq & 0xFFFFFF) - 1;
+    c.qm = (int)((uint32_t)pq >> 24);
+    c.abits = 0;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      if (c.pg >= 0 && (c.qm & mt_members[m]) != 0) c.abits |= 1 << m;
+    c.sc = lane_f(md_sc, l);
+    c.lvs = lane_f(md_lvs, l);
+    c.inv_vs = lane_f(md_ivs, l);
+    return c;
+  };
+
+  auto compute = [&](int t, auto stage_c, const PageCtx& pc) {
+    constexpr int SS = decltype(stage_c)::value;
+    const int pg = pc.pg, qm = pc.qm;
     const int tok0 = pg * p.page_size + (t & ((1 << tpp_shift) - 1)) * kTK;
     bool act[MT];
     bool any = false;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      act[m] = pg >= 0 && (qm & mt_members[m]) != 0 && tok0 <= mt_lim[m];
+      act[m] = ((pc.abits >> m) & 1) != 0 && tok0 <= mt_lim[m];
       any |= act[m];
     }
     if (!any) return;
-    const float sc = lane_f(md_sc, l);
-    const float lvs = lane_f(md_lvs, l);
-    const float inv_vs = lane_f(md_ivs, l);
+    const float sc = pc.sc;
+    const float lvs = pc.lvs;
+    const float inv_vs = pc.inv_vs;
     const PW_LDS uint8_t* st = lds_p + SS * C::kStageBytes;
 
     // K fragments (A operand of S^T = K . Q^T), shared by every row tile.  Held form:
@@ -780,21 +802,33 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
 
   // ---- pipeline: tile t lives in stage t % ST; the loop is unrolled by ST so that every
   // stage offset is a compile-time immediate ------------------------------------------------
-  auto step = [&](int t, auto stage_c) {
+  auto step = [&](int t, auto stage_c, const PageCtx& pc, int pg_next) {
     constexpr int SS = decltype(stage_c)::value;
     wait_tiles<C::kDmaPerTile, ST - 2>(min(n_tiles - 1 - t, ST - 2));   // tile t has landed
     if constexpr (NW > 1) __builtin_amdgcn_s_barrier();                 // ... for every wave
-    if (t + ST - 1 < n_tiles) issue(t + ST - 1, std::integral_constant<int, (SS + ST - 1) % ST>{});
-    compute(t, stage_c);
+    if (t + ST - 1 < n_tiles) issue(t + ST - 1, std::integral_constant<int, (SS + ST - 1) % ST>{}, pg_next);
+    compute(t, stage_c, pc);
   };
-  if (0 < n_tiles) issue(0, std::integral_constant<int, 0>{});
-  if constexpr (ST > 2) if (1 < n_tiles) issue(1, std::integral_constant<int, 1>{});
-  if constexpr (ST > 3) if (2 < n_tiles) issue(2, std::integral_constant<int, 2>{});
-  for (int t0 = 0; t0 < n_tiles; t0 += ST) {
-    step(t0, std::integral_constant<int, 0>{});
-    if (t0 + 1 < n_tiles) step(t0 + 1, std::integral_constant<int, 1>{});
-    if constexpr (ST > 2) if (t0 + 2 < n_tiles) step(t0 + 2, std::integral_constant<int, 2>{});
-    if constexpr (ST > 3) if (t0 + 3 < n_tiles) step(t0 + 3, std::integral_constant<int, 3>{});
+  if (0 < n_tiles) issue(0, std::integral_constant<int, 0>{}, kNoPage);
+  if constexpr (ST > 2) if (1 < n_tiles) issue(1, std::integral_constant<int, 1>{}, kNoPage);
+  if constexpr (ST > 3) if (2 < n_tiles) issue(2, std::integral_constant<int, 2>{}, kNoPage);
+  if constexpr (ST == 2) {
+    // a page holds 2 or 4 tiles and t0 is even, so tiles t0 and t0 + 1 share a page: its
+    // values are read once, and the load of tile t0 + 1 needs no page lookup
+    for (int t0 = 0; t0 < n_tiles; t0 += 2) {
+      const PageCtx pc = page_ctx(t0);
+      step(t0, std::integral_constant<int, 0>{}, pc, pc.pg);
+      if (t0 + 1 < n_tiles) step(t0 + 1, std::integral_constant<int, 1>{}, pc, kNoPage);
+    }
+  } else {
+    for (int t0 = 0; t0 < n_tiles; t0 += ST) {
+      step(t0, std::integral_constant<int, 0>{}, page_ctx(t0), kNoPage);
+      if (t0 + 1 < n_tiles) step(t0 + 1, std::integral_constant<int, 1>{}, page_ctx(t0 + 1), kNoPage);
+      if constexpr (ST > 2)
+        if (t0 + 2 < n_tiles) step(t0 + 2, std::integral_constant<int, 2>{}, page_ctx(t0 + 2), kNoPage);
+      if constexpr (ST > 3)
+        if (t0 + 3 < n_tiles) step(t0 + 3, std::integral_constant<int, 3>{}, page_ctx(t0 + 3), kNoPage);
+    }
   }
   wait_vmcnt<0>();
 
