@@ -872,8 +872,8 @@ pw_status launch_t(const Params& p, hipStream_t stream) {
 // <= 64 -> two waves of two row tiles.
 // Depth of the LDS tile ring.  The ring's LDS is what limits resident waves, and more
 // resident waves beat deeper prefetch: one-wave items use 2 stages (fp8 d=128: 16 KiB,
-// ten items per CU); items of 2 waves use 3, wider items 4.  PW_ATTN_STAGES (2, 3 or 4)
-// overrides it for tuning.
+// ten items per CU); items of 2 waves use 2 (3 for page-major items), wider items 4.
+// PW_ATTN_STAGES (2, 3 or 4) overrides it for tuning.
 template <int D, bool FP8, int MT, int NW>
 pw_status launch_nw(const Params& p, hipStream_t stream) {
   static const int env_st = [] {
@@ -881,7 +881,9 @@ pw_status launch_nw(const Params& p, hipStream_t stream) {
     const int v = e ? atoi(e) : 0;
     return (v >= 2 && v <= 4) ? v : 0;
   }();
-  const int st = env_st ? env_st : (NW == 1 ? 2 : (NW == 2 ? 3 : 4));
+  // two-wave items: 2 stages for tables of many pages (the two tiles of a page then share
+  // its values), 3 for page-major items (one page each, nothing to share)
+  const int st = env_st ? env_st : (NW == 1 ? 2 : (NW == 2 ? (p.item_kvh ? 3 : 2) : 4));
   if (st == 2) return launch_t<D, FP8, MT, NW, 2>(p, stream);
   if (st == 3) return launch_t<D, FP8, MT, NW, 3>(p, stream);
   return launch_t<D, FP8, MT, NW, 4>(p, stream);
