@@ -732,12 +732,11 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
         scores(bias0, pv, std::true_type{});
       // this lane's share of the row sum (its 8 of the tile's 32 keys); the four lanes of a
       // row are added up once, in the epilogue
-      float lsum = 0.f;
+      // (summed as a tree: three dependent adds instead of eight)
+      auto sum8 = [](const float* x) { return ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7])); };
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        pv[k] = __builtin_amdgcn_exp2f(pv[k]);
-        lsum += pv[k];
-      }
+      for (int k = 0; k < 8; ++k) pv[k] = __builtin_amdgcn_exp2f(pv[k]);
+      float lsum = sum8(pv);
       // The reference must be set (first used tile of a row) or raised (a lane's share of a
       // row sum passed 2^30, or overflowed): rare, wave-uniform slow path.  The decision is
       // made per row - lanes li, li+16, li+32 and li+48 hold row li - so that every key of
@@ -765,12 +764,9 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
         // fast-path values, so a row's arithmetic never depends on its tile-mates
         if (need) {
           const float bias = (sel && m_new != -INFINITY) ? lvs - m_new : -INFINITY;
-          lsum = 0.f;
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            pv[k] = __builtin_amdgcn_exp2f(raw[k] + bias);
-            lsum += pv[k];
-          }
+          for (int k = 0; k < 8; ++k) pv[k] = __builtin_amdgcn_exp2f(raw[k] + bias);
+          lsum = sum8(pv);
         }
       }
 #pragma unroll
