@@ -227,7 +227,7 @@ pw_status pw_prepare(const int32_t* topk, int nq, int hkv, int k, int n_pages, i
  * out         bf16 [nq][hq][d]; each row written exactly once if it belongs to
  *             a group; rows of queries in no group are left untouched
  * lse         fp32 [nq][hq] or NULL
- * Limits: d in {64, 128}; page_size in {64, 128}; hq % hkv == 0; n_pages >= 1;
+ * Limits: d in {64, 128}; page_size in {64, 128}; hq % hkv == 0; 1 <= n_pages <= 2^24 - 2;
  *   with group_qids or union_qmask: 1 <= max_group <= 8 and G * max_group <= 64;
  *   with neither (consecutive groups, every member uses every page of its table -
  *   the dense form over a shared per-KV-group table): max_group <= 256 and

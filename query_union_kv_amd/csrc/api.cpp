@@ -356,6 +356,8 @@ static pw_status check_sparse_prefill(const pw::AttnArgs& a, const char* who) {
     return fail(PW_ERR_ARG, "%s: bad sizes nq=%d hq=%d hkv=%d n_pages=%d n_groups=%d kv_len=%d", who,
                 a.nq, a.hq, a.hkv, a.n_pages, a.n_groups, a.kv_len);
   if (a.hq % a.hkv) return fail(PW_ERR_ARG, "%s: hq=%d not a multiple of hkv=%d", who, a.hq, a.hkv);
+  // the kernel packs page + 1 into 24 bits of a lane register
+  if (a.n_pages > (1 << 24) - 2) return fail(PW_ERR_UNSUPPORTED, "%s: n_pages=%d > 2^24 - 2", who, a.n_pages);
   if (a.d != 64 && a.d != 128) return fail(PW_ERR_UNSUPPORTED, "%s: d=%d (64 or 128)", who, a.d);
   if (a.page_size != 64 && a.page_size != 128)
     return fail(PW_ERR_UNSUPPORTED, "%s: page_size=%d (64 or 128)", who, a.page_size);

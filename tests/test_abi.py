@@ -109,6 +109,7 @@ def _attn(**kw):
     (dict(kv_dtype=2), -2), (dict(shared=2), -1), (dict(sp=100), -1),
     (dict(n_groups=0, nq=9), -1),                  # consecutive groups must cover nq
     (dict(sm=0.0), -1), (dict(nq=-1), -1),
+    (dict(n_pages=1 << 24), -2),                   # page IDs are packed into 24 bits
     (dict(), -1),                                  # null required pointers
 ])
 def test_attention_validation(kw, code):
