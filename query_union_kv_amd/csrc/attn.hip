@@ -448,8 +448,10 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     if (p.item_kvh) {
       // page-major items hold one page: every lane takes it through the scalar cache,
       // whose round trip is shorter than a vector load's on these two-tile items
-      pg = cpages[e_begin];
-      pg = (pg >= 0 && pg < p.n_pages) ? pg : -1;
+      if (e_begin < e_end) {   // (an empty table reads nothing)
+        pg = cpages[e_begin];
+        pg = (pg >= 0 && pg < p.n_pages) ? pg : -1;
+      }
       qm = 0xFF;
       if constexpr (FP8) {
         if (pg >= 0) {
@@ -471,7 +473,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
         }
       }
     }
-    md_pq = (pg + 1) | (qm << 24);   // n_pages <= 2^24 - 1
+    md_pq = (pg + 1) | (qm << 24);   // n_pages <= 2^24 - 2 (checked on the host)
     md_sc = p.score_scale * ks;                        // log2-domain score scale
     md_lvs = FP8 ? __builtin_amdgcn_logf(vs) : 0.f;    // log2 of the V page scale
     // 1 / vs only scales the row sums, so the hardware reciprocal (1 ulp) is ample
