@@ -645,6 +645,11 @@ __global__ __launch_bounds__(1024) void k_schedule(const int32_t* __restrict__ u
   for (int i = t; i < m; i += blockDim.x) order[lo + i] = (int32_t)(uint32_t)key[i];
 }
 
+// Lane l of a wave covers pages [64*w + 16*s, +16) of a 1024-page chunk, w = l / 4 and
+// s = l % 4 within the chunk, so that no lane lists more than 16 pages however closely
+// a union clusters (a whole 64-page word per lane left the wave waiting on lanes with
+// 40 and more pages of one community).  Lanes go in page order, so one exclusive scan
+// of the lane counts places every page.
 template <bool QMASK>
 __global__ void k_union_emit(const uint64_t* __restrict__ bits, int n_rows, int words,
                              const int32_t* __restrict__ group_rows,
@@ -658,37 +663,44 @@ __global__ void k_union_emit(const uint64_t* __restrict__ bits, int n_rows, int 
   const int g = e / n_groups;
   const int sz = member_count(group_size, e, group_width);
   const int32_t* rows = group_rows + (int64_t)e * group_width;
+  int r[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    r[j] = j < sz ? rows[j] : -1;
+    if (r[j] >= n_rows) r[j] = -1;   // (negative: no member)
+  }
+  const int sh = 16 * (lane & 3);
   int64_t pos = union_off[e];
-  for (int w0 = 0; w0 < words; w0 += kWave) {
-    const int w = w0 + lane;
-    uint64_t u = 0;
-    uint64_t mw[8];
+  for (int w0 = 0; w0 < words; w0 += kWave / 4) {
+    const int w = w0 + (lane >> 2);
+    uint32_t mw[8];
+    uint32_t u = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) mw[j] = 0;
-    if (w < words) {
-      for (int j = 0; j < sz; ++j) {
-        const int r = rows[j];
-        if (r < 0 || r >= n_rows) continue;
-        const uint64_t b = bits[((int64_t)g * n_rows + r) * words + w];
-        u |= b;
-        if (QMASK) {
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) if (jj == j) mw[jj] = b;
-        }
-      }
+    for (int j = 0; j < 8; ++j) {
+      mw[j] = 0u;
+      if (w < words && r[j] >= 0)
+        mw[j] = (uint32_t)(bits[((int64_t)g * n_rows + r[j]) * words + w] >> sh) & 0xFFFFu;
+      u |= mw[j];
     }
-    const int pc = __popcll(u);
+    if (!QMASK)   // (member masks need at most 8 members; plain tables take up to 64)
+      for (int j = 8; j < sz; ++j) {
+        const int rj = rows[j];
+        if (w < words && rj >= 0 && rj < n_rows)
+          u |= (uint32_t)(bits[((int64_t)g * n_rows + rj) * words + w] >> sh) & 0xFFFFu;
+      }
+    const int pc = __popc(u);
     int64_t p = pos + wave_excl_scan(pc, lane);
     const int chunk_total = wave_sum(pc);
+    const int base = w * 64 + sh;
     while (u) {
-      const int b = __ffsll((unsigned long long)u) - 1;
+      const int b = __ffs(u) - 1;
       u &= u - 1;
       if (p < capacity) {
-        union_pages[p] = w * 64 + b;
+        union_pages[p] = base + b;
         if (QMASK) {
           int qm = 0;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) qm |= (int)((mw[j] >> b) & 1ull) << j;
+          for (int j = 0; j < 8; ++j) qm |= (int)((mw[j] >> b) & 1u) << j;
           union_qmask[p] = (uint8_t)qm;
         }
       }
