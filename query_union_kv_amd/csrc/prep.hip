@@ -290,12 +290,16 @@ __global__ __launch_bounds__(64) void k_group_wave(const uint64_t* __restrict__ 
 // listing remain.  Results are identical to the three separate steps.
 //  * bitsets: the window's rows live in LDS (64 x 1024 bits); every valid ID sets its bit
 //    with an LDS atomic OR, and the rows are copied out to `bits`;
-//  * grouping: wave v scores words [4v, 4v+4) of every candidate (lane = candidate) and the
-//    partial overlaps are summed through LDS, so the pick chain is split over up to four
-//    waves; the argmax key and the union U follow the single-wave search exactly.
-constexpr int kFusedWordsPerWave = 4;
+//  * grouping: wave v scores words [2v, 2v+2) of every candidate (lane = candidate) and the
+//    partial overlaps are summed through LDS, so the pick chain is split over up to eight
+//    waves; the argmax key and the union U follow the single-wave search exactly.  (Per
+//    pick, the barrier costs less than the popcounts it splits: on the 64K fp8 Top16
+//    tables one wave took 7 us longer and two waves 11 us longer than four; eight match
+//    four there and gain 3 us where a window spans four words.)
+constexpr int kFusedWordsPerWave = 2;
+constexpr int kFusedMaxWaves = 16 / kFusedWordsPerWave;   // 1024 pages
 
-__global__ __launch_bounds__(256) void k_prepare(const int32_t* __restrict__ topk, int nq, int hkv,
+__global__ __launch_bounds__(64 * kFusedMaxWaves) void k_prepare(const int32_t* __restrict__ topk, int nq, int hkv,
                                                  int k, int n_pages, int words, int window,
                                                  int max_group, int n_groups,
                                                  uint64_t* __restrict__ bits,
@@ -304,10 +308,10 @@ __global__ __launch_bounds__(256) void k_prepare(const int32_t* __restrict__ top
                                                  int32_t* __restrict__ group_size,
                                                  int32_t* __restrict__ union_count) {
   __shared__ uint32_t rows[64][33];                    // +1 dword per row against bank conflicts
-  // per-candidate partial scores of the (up to 4) waves, lane-major so that one 16-byte
-  // read gathers them; two buffers, alternating per pick, so one barrier per pick suffices
-  __shared__ __attribute__((aligned(16))) int part[2][64][4];
-  __shared__ int red[4];
+  // per-candidate partial scores of the (up to 8) waves, lane-major so that two 16-byte
+  // reads gather them; two buffers, alternating per pick, so one barrier per pick suffices
+  __shared__ __attribute__((aligned(16))) int part[2][64][kFusedMaxWaves];
+  __shared__ int red[kFusedMaxWaves];
   const int g = blockIdx.y;
   const int start = blockIdx.x * window;
   const int len = min(window, nq - start);
@@ -349,7 +353,7 @@ __global__ __launch_bounds__(256) void k_prepare(const int32_t* __restrict__ top
   int gi = 0;
   int pb = 0;   // partial-score buffer of the next pick
   if (nwaves > 1)
-    for (int i = tid; i < 2 * 64 * 4; i += blockDim.x) (&part[0][0][0])[i] = 0;
+    for (int i = tid; i < 2 * 64 * kFusedMaxWaves; i += blockDim.x) (&part[0][0][0])[i] = 0;
   __syncthreads();
   while (free_mask) {
     const int seed = __builtin_ctzll(free_mask);
@@ -375,7 +379,8 @@ __global__ __launch_bounds__(256) void k_prepare(const int32_t* __restrict__ top
         part[pb][lane][wave] = partial;
         __syncthreads();
         const int4 ps = *reinterpret_cast<const int4*>(&part[pb][lane][0]);
-        score = ps.x + ps.y + ps.z + ps.w;   // unused waves' slots stay 0
+        const int4 pt = *reinterpret_cast<const int4*>(&part[pb][lane][4]);
+        score = (ps.x + ps.y + ps.z + ps.w) + (pt.x + pt.y + pt.z + pt.w);   // unused slots stay 0
         pb ^= 1;
       }
       const bool is_free = (free_mask >> lane) & 1ull;
