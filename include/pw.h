@@ -183,11 +183,15 @@ pw_status pw_union_tables(const uint64_t* bits, int n_rows, int hkv, int n_pages
  * window's bitsets, groups it and sizes its unions (then a prefix sum and the union
  * listing follow); other shapes run the three steps.  Arguments and limits as in the
  * three calls; union_qmask is required; capacity >= pw_union_capacity(hkv*G,
- * max_group, k, n_pages) with G = pw_num_groups(nq, window, max_group).            */
+ * max_group, k, n_pages) with G = pw_num_groups(nq, window, max_group).
+ * item_order   int32 [hkv*G] output or NULL: when given, also the work order of
+ *              pw_schedule_items(union_off, hkv*G, item_order), computed in the union
+ *              listing's launch (the same values as the separate call).               */
 pw_status pw_prepare(const int32_t* topk, int nq, int hkv, int k, int n_pages, int window,
                      int max_group, uint64_t* bits, int32_t* bad_id_count, int32_t* group_qids,
                      int32_t* group_size, int32_t* union_off, int32_t* union_pages,
-                     uint8_t* union_qmask, int64_t capacity, hipStream_t stream);
+                     uint8_t* union_qmask, int64_t capacity, int32_t* item_order,
+                     hipStream_t stream);
 
 /* ---- (4) ID-aware union attention -----------------------------------------------------
  * PageWeaver abstract, Fig. 1 and Fig. 3: each group's union pages are staged

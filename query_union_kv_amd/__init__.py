@@ -63,7 +63,7 @@ def lib() -> ctypes.CDLL:
             "pw_group": (I, [P, I, I, I, I, I, P, P, P]),
             "pw_union_tables": (I, [P, I, I, I, P, P, I, I, I, P, P, P, I64, P]),
             "pw_arrange_groups": (I, [P, I, I, I, I, I, I, P, P, P, P, I64, P]),
-            "pw_prepare": (I, [P, I, I, I, I, I, I, P, P, P, P, P, P, P, I64, P]),
+            "pw_prepare": (I, [P, I, I, I, I, I, I, P, P, P, P, P, P, P, I64, P, P]),
             "pw_sparse_prefill": (I, [P, I, I, I, I, P, P, I, P, P, I, I, I64, I64, P, I, F,
                                       P, P, I, I, I, P, P, P, I64, P, P, P, P]),
             "pw_schedule_items": (I, [P, I, P, P]),
@@ -228,10 +228,14 @@ def pw_union_tables(bits: torch.Tensor, n_pages: int, group_rows: torch.Tensor,
 def pw_prepare(topk: torch.Tensor, n_pages: int, window: int, max_group: int,
                bits: torch.Tensor, group_qids: torch.Tensor, group_size: torch.Tensor,
                union_off: torch.Tensor, union_pages: torch.Tensor, union_qmask: torch.Tensor,
-               bad_id_count: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Fused pw_page_bitsets + pw_group + pw_union_tables (same outputs)."""
+               bad_id_count: Optional[torch.Tensor] = None, stream=None,
+               item_order: Optional[torch.Tensor] = None) -> None:
+    """Fused pw_page_bitsets + pw_group + pw_union_tables (same outputs); with item_order,
+    also the work order of pw_schedule_items."""
     nq, hkv, k = topk.shape
     n_groups = pw_num_groups(nq, window, max_group)
+    if item_order is not None and item_order.numel() != hkv * n_groups:
+        raise ValueError("item_order must hold one entry per union table")
     if tuple(bits.shape) != (hkv, nq, pw_words(n_pages)):
         raise ValueError("bits shape")
     if tuple(group_qids.shape) != (hkv, n_groups, max_group) or tuple(group_size.shape) != (hkv, n_groups):
@@ -246,7 +250,8 @@ def pw_prepare(topk: torch.Tensor, n_pages: int, window: int, max_group: int,
                             _ptr(union_off, torch.int32, "union_off"),
                             _ptr(union_pages, torch.int32, "union_pages"),
                             _ptr(union_qmask, torch.uint8, "union_qmask"),
-                            union_pages.numel(), _stream(stream)))
+                            union_pages.numel(), _ptr(item_order, torch.int32, "item_order"),
+                            _stream(stream)))
 
 
 def pw_sparse_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -527,14 +532,13 @@ class SparsePrefill:
     def prepare(self, ids: torch.Tensor, stream=None) -> None:
         """Bitsets, grouping and union tables from topk [nq, hkv, k] or mask rows [n_rows, hkv, k]."""
         if self.mode == "topk" and self.grouping == "affinity" and self.fused:
+            # (the work order comes with the tables; arranging members keeps union sizes)
             pw_prepare(ids, self.n_pages, self.window, self.max_group, self.bits, self.group_qids,
                        self.group_size, self.union_off, self.union_pages, self.union_qmask,
-                       self.bad_ids, stream)
+                       self.bad_ids, stream, item_order=self.item_order)
             if self.arrange:
                 pw_arrange_groups(self.bits, self.n_pages, self.hq, self.group_qids, self.group_size,
                                   self.union_off, self.union_qmask, stream)
-            if self.item_order is not None:
-                pw_schedule_items(self.union_off, self.item_order, stream)
             return
         pw_page_bitsets(ids, self.n_pages, self.bits, self.bad_ids, stream)
         if self.mode == "topk":

@@ -189,7 +189,8 @@ pw_status pw_union_tables(const uint64_t* bits, int n_rows, int hkv, int n_pages
 pw_status pw_prepare(const int32_t* topk, int nq, int hkv, int k, int n_pages, int window,
                      int max_group, uint64_t* bits, int32_t* bad_id_count, int32_t* group_qids,
                      int32_t* group_size, int32_t* union_off, int32_t* union_pages,
-                     uint8_t* union_qmask, int64_t capacity, hipStream_t stream) {
+                     uint8_t* union_qmask, int64_t capacity, int32_t* item_order,
+                     hipStream_t stream) {
   pw::g_err[0] = 0;
   if (nq < 0 || hkv < 1 || k < 1 || n_pages < 1)
     return fail(PW_ERR_ARG, "pw_prepare: bad sizes nq=%d hkv=%d k=%d n_pages=%d", nq, hkv, k, n_pages);
@@ -218,7 +219,7 @@ pw_status pw_prepare(const int32_t* topk, int nq, int hkv, int k, int n_pages, i
   if (pw::prepare_fusable(n_pages, window))
     return pw::launch_prepare(topk, nq, hkv, k, n_pages, window, max_group, n_groups, bits,
                               bad_id_count, group_qids, group_size, union_off, union_pages,
-                              union_qmask, capacity, stream);
+                              union_qmask, capacity, item_order, stream);
   pw_status st = pw::launch_page_bitsets(topk, nq, hkv, k, n_pages, bits, bad_id_count, stream);
   if (st == PW_OK)
     st = pw::launch_group(bits, nq, hkv, n_pages, window, max_group, n_groups, group_qids,
@@ -226,6 +227,8 @@ pw_status pw_prepare(const int32_t* topk, int nq, int hkv, int k, int n_pages, i
   if (st == PW_OK)
     st = pw::launch_union_tables(bits, nq, hkv, n_pages, group_qids, group_size, n_groups,
                                  max_group, union_off, union_pages, union_qmask, capacity, stream);
+  if (st == PW_OK && item_order)
+    st = pw::launch_schedule(union_off, hkv * n_groups, item_order, stream);
   return st;
 }
 

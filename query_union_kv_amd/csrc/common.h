@@ -33,13 +33,14 @@ pw_status launch_union_tables(const uint64_t* bits, int n_rows, int hkv, int n_p
                               int group_width, int32_t* union_off, int32_t* union_pages,
                               uint8_t* union_qmask, int64_t capacity, hipStream_t stream);
 
-// Fused bitsets + grouping + union tables (windows <= 64, n_pages <= 1024).
+// Fused bitsets + grouping + union tables (windows <= 64, n_pages <= 1024), and the
+// work order of pw_schedule_items when item_order is not NULL.
 bool prepare_fusable(int n_pages, int window);
 pw_status launch_prepare(const int32_t* topk, int nq, int hkv, int k, int n_pages, int window,
                          int max_group, int n_groups, uint64_t* bits, int32_t* bad_id_count,
                          int32_t* group_qids, int32_t* group_size, int32_t* union_off,
                          int32_t* union_pages, uint8_t* union_qmask, int64_t capacity,
-                         hipStream_t stream);
+                         int32_t* item_order, hipStream_t stream);
 
 // Member order of 5..8-member groups for 4-member row tiles, with member-mask bits to match.
 pw_status launch_arrange(const uint64_t* bits, int nq, int hkv, int n_pages, int n_groups,

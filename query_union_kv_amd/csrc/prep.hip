@@ -591,11 +591,12 @@ __global__ void k_union_scan(int32_t* __restrict__ union_off, int n) {
 // up to 1024 items hold one 32-bit key per thread and exchange partners with lane
 // shuffles (distance < 64) or through LDS (distance >= 64); longer ranges, up to
 // kScheduleCap, sort 64-bit keys in LDS; a range longer than that keeps item order.
+// `key` is LDS for schedule_lds_bytes(per) bytes; the workgroup has at least
+// min(1024, N) threads, N = per rounded up to a power of two >= 64.
 constexpr int kScheduleCap = 8192;
-__global__ __launch_bounds__(1024) void k_schedule(const int32_t* __restrict__ union_off, int n,
-                                                   int per, int32_t* __restrict__ order) {
-  __shared__ uint64_t key[kScheduleCap];
-  const int lo = blockIdx.x * per;
+__device__ void schedule_range(const int32_t* __restrict__ union_off, int n, int per, int range,
+                               int32_t* __restrict__ order, uint64_t* key) {
+  const int lo = range * per;
   const int m = min(n, lo + per) - lo;
   if (m <= 0) return;
   const int t = threadIdx.x;
@@ -650,20 +651,38 @@ __global__ __launch_bounds__(1024) void k_schedule(const int32_t* __restrict__ u
   for (int i = t; i < m; i += blockDim.x) order[lo + i] = (int32_t)(uint32_t)key[i];
 }
 
+__host__ __device__ constexpr int schedule_keys(int per) {
+  int N = 64;
+  while (N < per) N <<= 1;
+  return N;
+}
+__host__ __device__ constexpr int schedule_threads(int per) {
+  return schedule_keys(per) < 1024 ? schedule_keys(per) : 1024;
+}
+// LDS for any range of m <= per items: 4 N(m) bytes up to 1024 keys, else 8 N(m) while
+// m <= kScheduleCap (a shorter last range may sort where the others keep item order)
+__host__ __device__ constexpr int schedule_lds_bytes(int per) {
+  return per <= 1024 ? 4 * schedule_keys(per) : 8 * schedule_keys(per < kScheduleCap ? per : kScheduleCap);
+}
+
+__global__ __launch_bounds__(1024) void k_schedule(const int32_t* __restrict__ union_off, int n,
+                                                   int per, int32_t* __restrict__ order) {
+  extern __shared__ uint64_t sched_key[];
+  schedule_range(union_off, n, per, blockIdx.x, order, sched_key);
+}
+
 // Lane l of a wave covers pages [64*w + 16*s, +16) of a 1024-page chunk, w = l / 4 and
 // s = l % 4 within the chunk, so that no lane lists more than 16 pages however closely
 // a union clusters (a whole 64-page word per lane left the wave waiting on lanes with
 // 40 and more pages of one community).  Lanes go in page order, so one exclusive scan
 // of the lane counts places every page.
 template <bool QMASK>
-__global__ void k_union_emit(const uint64_t* __restrict__ bits, int n_rows, int words,
-                             const int32_t* __restrict__ group_rows,
-                             const int32_t* __restrict__ group_size, int n_groups, int n_tables,
-                             int group_width, const int32_t* __restrict__ union_off,
-                             int32_t* __restrict__ union_pages, uint8_t* __restrict__ union_qmask,
-                             int64_t capacity) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int e = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+__device__ void emit_table(const uint64_t* __restrict__ bits, int n_rows, int words,
+                           const int32_t* __restrict__ group_rows,
+                           const int32_t* __restrict__ group_size, int n_groups, int n_tables,
+                           int group_width, const int32_t* __restrict__ union_off,
+                           int32_t* __restrict__ union_pages, uint8_t* __restrict__ union_qmask,
+                           int64_t capacity, int e, int lane) {
   if (e >= n_tables) return;
   const int g = e / n_groups;
   const int sz = member_count(group_size, e, group_width);
@@ -715,6 +734,37 @@ __global__ void k_union_emit(const uint64_t* __restrict__ bits, int n_rows, int 
   }
 }
 
+
+template <bool QMASK>
+__global__ void k_union_emit(const uint64_t* __restrict__ bits, int n_rows, int words,
+                             const int32_t* __restrict__ group_rows,
+                             const int32_t* __restrict__ group_size, int n_groups, int n_tables,
+                             int group_width, const int32_t* __restrict__ union_off,
+                             int32_t* __restrict__ union_pages, uint8_t* __restrict__ union_qmask,
+                             int64_t capacity) {
+  emit_table<QMASK>(bits, n_rows, words, group_rows, group_size, n_groups, n_tables, group_width,
+                    union_off, union_pages, union_qmask, capacity,
+                    blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave, threadIdx.x & (kWave - 1));
+}
+
+// The union listing and the work order in one launch (both only read the prefix sums):
+// workgroups 0..7 sort the 8 ranges, the others list blockDim / 64 tables each.
+__global__ __launch_bounds__(1024) void k_union_emit_schedule(
+    const uint64_t* __restrict__ bits, int n_rows, int words, const int32_t* __restrict__ group_rows,
+    const int32_t* __restrict__ group_size, int n_groups, int n_tables, int group_width,
+    const int32_t* __restrict__ union_off, int32_t* __restrict__ union_pages,
+    uint8_t* __restrict__ union_qmask, int64_t capacity, int per, int32_t* __restrict__ order) {
+  extern __shared__ uint64_t sched_key[];
+  if (blockIdx.x < 8) {   // (uniform over the workgroup: its barriers are all reached)
+    schedule_range(union_off, n_tables, per, blockIdx.x, order, sched_key);
+    return;
+  }
+  emit_table<true>(bits, n_rows, words, group_rows, group_size, n_groups, n_tables, group_width,
+                   union_off, union_pages, union_qmask, capacity,
+                   (blockIdx.x - 8) * (blockDim.x / kWave) + threadIdx.x / kWave,
+                   threadIdx.x & (kWave - 1));
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
@@ -733,9 +783,8 @@ pw_status launch_arrange(const uint64_t* bits, int nq, int hkv, int n_pages, int
 pw_status launch_schedule(const int32_t* union_off, int n, int32_t* order, hipStream_t stream) {
   if (n <= 0) return PW_OK;
   const int per = (n + 7) / 8;
-  int threads = 64;   // one thread per key up to 1024 keys per range
-  while (threads < per && threads < 1024) threads <<= 1;
-  hipLaunchKernelGGL(k_schedule, dim3(8), dim3(threads), 0, stream, union_off, n, per, order);
+  hipLaunchKernelGGL(k_schedule, dim3(8), dim3(schedule_threads(per)), schedule_lds_bytes(per),
+                     stream, union_off, n, per, order);
   return check_launch("schedule_items");
 }
 
@@ -812,7 +861,7 @@ pw_status launch_prepare(const int32_t* topk, int nq, int hkv, int k, int n_page
                          int max_group, int n_groups, uint64_t* bits, int32_t* bad_id_count,
                          int32_t* group_qids, int32_t* group_size, int32_t* union_off,
                          int32_t* union_pages, uint8_t* union_qmask, int64_t capacity,
-                         hipStream_t stream) {
+                         int32_t* item_order, hipStream_t stream) {
   const int words = (n_pages + 63) / 64;
   const int n_tables = hkv * n_groups;
   if (nq > 0) {
@@ -826,6 +875,16 @@ pw_status launch_prepare(const int32_t* topk, int nq, int hkv, int k, int n_page
   hipLaunchKernelGGL(k_union_scan, dim3(1), dim3(1024), 0, stream, union_off, n_tables);
   pw_status st = check_launch("union_scan");
   if (st != PW_OK || n_tables == 0) return st;
+  if (item_order) {
+    const int per = (n_tables + 7) / 8;
+    const int threads = schedule_threads(per);
+    const int wpb = threads / kWave;
+    hipLaunchKernelGGL(k_union_emit_schedule, dim3(8 + (n_tables + wpb - 1) / wpb), dim3(threads),
+                       schedule_lds_bytes(per), stream, bits, nq, words, group_qids, group_size,
+                       n_groups, n_tables, max_group, union_off, union_pages, union_qmask, capacity,
+                       per, item_order);
+    return check_launch("union_emit_schedule");
+  }
   const int wpb = 4;
   const int blocks = (n_tables + wpb - 1) / wpb;
   hipLaunchKernelGGL(k_union_emit<true>, dim3(blocks), dim3(wpb * kWave), 0, stream, bits, nq,

@@ -59,6 +59,8 @@ def run_gpu(w, grouping="affinity", window=None, max_group=None, with_lse=True, 
         res["union_qmask"] = plan.union_qmask[:total].cpu().numpy()
         res["group_qids"] = plan.group_qids.cpu().numpy()
         res["group_size"] = plan.group_size.cpu().numpy()
+    if getattr(plan, "item_order", None) is not None:
+        res["item_order"] = plan.item_order.cpu().numpy()
     if with_lse:
         res["lse"] = lse.cpu().numpy()
     return res, plan

@@ -144,12 +144,13 @@ def test_binding_rejects_host_tensors():
 
 
 @pytest.mark.parametrize("args,code", [
-    # topk, nq, hkv, k, n_pages, window, mg, bits, bad, qids, size, off, pages, qmask, cap, stream
-    ((NULL, 64, 1, 4, 16, 64, 9, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 512, NULL), -2),  # mg 9
-    ((NULL, 64, 1, 4, 16, 60, 8, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 512, NULL), -1),  # W % mg
-    ((NULL, 64, 1, 4, 5000, 64, 8, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 512, NULL), -2),  # pages
-    ((NULL, 64, 1, 4, 16, 64, 8, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 127, NULL), -3),  # capacity
-    ((NULL, 64, 1, 4, 16, 64, 8, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 128, NULL), -1),  # nulls
+    # topk, nq, hkv, k, n_pages, window, mg, bits, bad, qids, size, off, pages, qmask, cap, order,
+    # stream
+    ((NULL, 64, 1, 4, 16, 64, 9, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 512, NULL, NULL), -2),  # mg 9
+    ((NULL, 64, 1, 4, 16, 60, 8, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 512, NULL, NULL), -1),  # W % mg
+    ((NULL, 64, 1, 4, 5000, 64, 8, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 512, NULL, NULL), -2),  # pages
+    ((NULL, 64, 1, 4, 16, 64, 8, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 127, NULL, NULL), -3),  # capacity
+    ((NULL, 64, 1, 4, 16, 64, 8, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 128, NULL, NULL), -1),  # nulls
 ])
 def test_prepare_validation(args, code):
     st, msg = _err(L.pw_prepare(*args))

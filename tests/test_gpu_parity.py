@@ -168,7 +168,8 @@ def test_fused_prepare_equals_separate_steps(kw):
     w.topk = add_padding_and_duplicates(w.topk, seed=cfg.seed + 1)
     a, _ = run_gpu(w, fused=True)
     b, _ = run_gpu(w, fused=False)
-    for key in ("bits", "group_qids", "group_size", "union_off", "union_pages", "union_qmask", "out"):
+    for key in ("bits", "group_qids", "group_size", "union_off", "union_pages", "union_qmask",
+                "item_order", "out"):
         assert np.array_equal(a[key], b[key]), key
     _compare_tables(a, oracle_tables(w))
 
@@ -270,11 +271,12 @@ def test_fp8_query_dynamic_range(hq, hkv):
     print(f"[parity] fp8 dynamic range hq={hq}: max_abs={mx:.3e} mean_abs={mean:.3e}", flush=True)
 
 
-@pytest.mark.parametrize("n", [1, 7, 8, 9, 100, 513, 4096, 8192, 8200, 65536, 65600])
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 100, 513, 4096, 8192, 8200, 65536, 65537, 65600])
 def test_work_order_matches_oracle(n):
     """pw_schedule_items against the oracle's work order on synthetic union sizes: ranges
-    of <= 1024 items (one key per thread), longer ones (keys in LDS) and, at 65600 items,
-    ranges of 8200 > 8192 that keep item order."""
+    of <= 1024 items (one key per thread), longer ones (keys in LDS), at 65600 items
+    ranges of 8200 > 8192 that keep item order, and at 65537 seven such ranges of 8193
+    beside a last one of 8186 that is sorted."""
     rng = np.random.default_rng(n)
     sizes = rng.integers(0, 130, size=n).astype(np.int64)
     sizes[rng.random(n) < 0.2] = 64                       # many ties
@@ -282,6 +284,34 @@ def test_work_order_matches_oracle(n):
     off[1:] = np.cumsum(sizes)
     order = torch.full((n,), -7, dtype=torch.int32, device="cuda")
     pw.pw_schedule_items(torch.from_numpy(off).cuda(), order)
+    assert np.array_equal(order.cpu().numpy(), np.array(prep.work_order(sizes.tolist()), dtype=np.int32))
+
+
+@pytest.mark.parametrize("nq,max_group", [(9, 8), (700, 1), (9000, 1), (65537, 1), (66000, 1)])
+def test_prepare_work_order(nq, max_group):
+    """pw_prepare's work order (listed in the union listing's launch) equals pw_schedule_items
+    on the same tables and the oracle's: ranges of <= 1024 tables, longer ones (keys in
+    LDS), at 66000 tables ranges of 8250 > 8192 that keep item order, and at 65537 a last
+    range of 8186 that is sorted beside seven of 8193 that are not."""
+    rng = np.random.default_rng(nq)
+    n_pages, k, window = 64, 3, 64
+    print(f"[parity] prepare work order nq={nq} max_group={max_group}", flush=True)
+    topk = torch.from_numpy(rng.integers(-1, n_pages, size=(nq, 1, k)).astype(np.int32)).cuda()
+    G = pw.pw_num_groups(nq, window, max_group)
+    cap = pw.pw_union_capacity(G, max_group, k, n_pages)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    bits = torch.empty((1, nq, pw.pw_words(n_pages)), dtype=torch.int64, device="cuda")
+    qids, size = torch.empty((1, G, max_group), **i32), torch.empty((1, G), **i32)
+    off, pages = torch.empty(G + 1, **i32), torch.empty(cap, **i32)
+    qmask = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    order = torch.full((G,), -7, **i32)
+    pw.pw_prepare(topk, n_pages, window, max_group, bits, qids, size, off, pages, qmask,
+                  item_order=order)
+    order2 = torch.full((G,), -7, **i32)
+    pw.pw_schedule_items(off, order2)
+    torch.cuda.synchronize()
+    sizes = np.diff(off.cpu().numpy().astype(np.int64))
+    assert np.array_equal(order.cpu().numpy(), order2.cpu().numpy())
     assert np.array_equal(order.cpu().numpy(), np.array(prep.work_order(sizes.tolist()), dtype=np.int32))
 
 
