@@ -298,6 +298,7 @@ __global__ __launch_bounds__(64) void k_group_wave(const uint64_t* __restrict__ 
 //    four there and gain 3 us where a window spans four words.)
 constexpr int kFusedWordsPerWave = 2;
 constexpr int kFusedMaxWaves = 16 / kFusedWordsPerWave;   // 1024 pages
+static_assert(kFusedMaxWaves == 8, "the partial scores are summed as a tree of eight");
 
 __global__ __launch_bounds__(64 * kFusedMaxWaves) void k_prepare(const int32_t* __restrict__ topk, int nq, int hkv,
                                                  int k, int n_pages, int words, int window,
@@ -308,10 +309,11 @@ __global__ __launch_bounds__(64 * kFusedMaxWaves) void k_prepare(const int32_t* 
                                                  int32_t* __restrict__ group_size,
                                                  int32_t* __restrict__ union_count) {
   __shared__ uint32_t rows[64][33];                    // +1 dword per row against bank conflicts
-  // per-candidate partial scores of the (up to 8) waves, lane-major so that two 16-byte
-  // reads gather them; two buffers, alternating per pick, so one barrier per pick suffices
-  __shared__ __attribute__((aligned(16))) int part[2][64][kFusedMaxWaves];
-  __shared__ int red[kFusedMaxWaves];
+  // per-candidate partial scores of the (up to 8) waves, wave-major so that the writes
+  // and the reads (stride 64 dwords) are free of bank conflicts; two buffers, alternating
+  // per pick, so one barrier per pick suffices
+  __shared__ int part[2][kFusedMaxWaves][64];
+  __shared__ int usz_acc[64];   // union size of each of the window's (<= 64) groups
   const int g = blockIdx.y;
   const int start = blockIdx.x * window;
   const int len = min(window, nq - start);
@@ -354,6 +356,7 @@ __global__ __launch_bounds__(64 * kFusedMaxWaves) void k_prepare(const int32_t* 
   int pb = 0;   // partial-score buffer of the next pick
   if (nwaves > 1)
     for (int i = tid; i < 2 * 64 * kFusedMaxWaves; i += blockDim.x) (&part[0][0][0])[i] = 0;
+  for (int i = tid; i < 64; i += blockDim.x) usz_acc[i] = 0;
   __syncthreads();
   while (free_mask) {
     const int seed = __builtin_ctzll(free_mask);
@@ -376,11 +379,12 @@ __global__ __launch_bounds__(64 * kFusedMaxWaves) void k_prepare(const int32_t* 
       if (nwaves > 1) {
         // a wave rewrites buffer pb only two picks later, after every wave has passed the
         // barrier of the pick in between (and so has read this pick's partials)
-        part[pb][lane][wave] = partial;
+        part[pb][wave][lane] = partial;
         __syncthreads();
-        const int4 ps = *reinterpret_cast<const int4*>(&part[pb][lane][0]);
-        const int4 pt = *reinterpret_cast<const int4*>(&part[pb][lane][4]);
-        score = (ps.x + ps.y + ps.z + ps.w) + (pt.x + pt.y + pt.z + pt.w);   // unused slots stay 0
+        int ps[kFusedMaxWaves];
+#pragma unroll
+        for (int v = 0; v < kFusedMaxWaves; ++v) ps[v] = part[pb][v][lane];   // unused slots stay 0
+        score = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
         pb ^= 1;
       }
       const bool is_free = (free_mask >> lane) & 1ull;
@@ -396,17 +400,12 @@ __global__ __launch_bounds__(64 * kFusedMaxWaves) void k_prepare(const int32_t* 
       for (int j = 1; j < 8; ++j) if (j == cnt) members[j] = pick;
       ++cnt;
     }
-    // union size: popcount of U over every wave's words
+    // union size: popcount of U over every wave's words, summed by LDS atomics (read
+    // after the loop, so no barrier per group)
     int usz = 0;
 #pragma unroll
     for (int i = 0; i < kFusedWordsPerWave; ++i) usz += __builtin_popcount(ulo[i]) + __builtin_popcount(uhi[i]);
-    if (nwaves > 1) {
-      if (lane == 0) red[wave] = usz;
-      __syncthreads();
-      usz = 0;
-      for (int v = 0; v < nwaves; ++v) usz += red[v];
-      __syncthreads();
-    }
+    if (lane == 0) atomicAdd(&usz_acc[gi], usz);
     if (wave == 0) {
       if (lane < max_group) {
         int v = -1;
@@ -414,13 +413,12 @@ __global__ __launch_bounds__(64 * kFusedMaxWaves) void k_prepare(const int32_t* 
         for (int j = 0; j < 8; ++j) if (j == lane && j < cnt) v = start + members[j];
         group_qids[(gbase + gi) * max_group + lane] = v;
       }
-      if (lane == 0) {
-        group_size[gbase + gi] = cnt;
-        union_count[gbase + gi + 1] = usz;
-      }
+      if (lane == 0) group_size[gbase + gi] = cnt;
     }
     ++gi;
   }
+  __syncthreads();   // (every wave made the same picks, so all arrive here)
+  if (tid < gi) union_count[gbase + tid + 1] = usz_acc[tid];
 }
 
 // ---------------------------------------------------------------------------------------
