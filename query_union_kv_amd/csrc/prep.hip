@@ -292,22 +292,19 @@ __global__ __launch_bounds__(64) void k_group_wave(const uint64_t* __restrict__ 
 //    with an LDS atomic OR, and the rows are copied out to `bits`;
 //  * grouping: wave v scores words [2v, 2v+2) of every candidate (lane = candidate) and the
 //    partial overlaps are summed through LDS, so the pick chain is split over up to eight
-//    waves; the argmax key and the union U follow the single-wave search exactly.  (Per
-//    pick, the barrier costs less than the popcounts it splits: on the 64K fp8 Top16
-//    tables one wave took 7 us longer and two waves 11 us longer than four; eight match
-//    four there and gain 3 us where a window spans four words.)
+//    waves; the argmax key and the union U follow the single-wave search exactly.
+//    (Measured on the 64K fp8 Top16 tables: one wave per window took 7 us longer and two
+//    waves 11 us longer than four; eight match four there and gain 3 us where a window
+//    spans four words.)
 constexpr int kFusedWordsPerWave = 2;
 constexpr int kFusedMaxWaves = 16 / kFusedWordsPerWave;   // 1024 pages
 static_assert(kFusedMaxWaves == 8, "the partial scores are summed as a tree of eight");
 
-__global__ __launch_bounds__(64 * kFusedMaxWaves) void k_prepare(const int32_t* __restrict__ topk, int nq, int hkv,
-                                                 int k, int n_pages, int words, int window,
-                                                 int max_group, int n_groups,
-                                                 uint64_t* __restrict__ bits,
-                                                 int32_t* __restrict__ bad_id_count,
-                                                 int32_t* __restrict__ group_qids,
-                                                 int32_t* __restrict__ group_size,
-                                                 int32_t* __restrict__ union_count) {
+__global__ __launch_bounds__(64 * kFusedMaxWaves) void k_prepare(
+    const int32_t* __restrict__ topk, int nq, int hkv, int k, int n_pages, int words, int window,
+    int max_group, int n_groups, uint64_t* __restrict__ bits, int32_t* __restrict__ bad_id_count,
+    int32_t* __restrict__ group_qids, int32_t* __restrict__ group_size,
+    int32_t* __restrict__ union_count) {
   __shared__ uint32_t rows[64][33];                    // +1 dword per row against bank conflicts
   // per-candidate partial scores of the (up to 8) waves, wave-major so that the writes
   // and the reads (stride 64 dwords) are free of bank conflicts; two buffers, alternating
@@ -590,7 +587,8 @@ __global__ void k_union_scan(int32_t* __restrict__ union_off, int n) {
 // shuffles (distance < 64) or through LDS (distance >= 64); longer ranges, up to
 // kScheduleCap, sort 64-bit keys in LDS; a range longer than that keeps item order.
 // `key` is LDS for schedule_lds_bytes(per) bytes; the workgroup has at least
-// min(1024, N) threads, N = per rounded up to a power of two >= 64.
+// min(1024, N) threads, N = per rounded up to a power of two >= 64, and every thread of
+// it calls this (the ranges' sorts hold barriers).
 constexpr int kScheduleCap = 8192;
 __device__ void schedule_range(const int32_t* __restrict__ union_off, int n, int per, int range,
                                int32_t* __restrict__ order, uint64_t* key) {
@@ -605,11 +603,12 @@ __device__ void schedule_range(const int32_t* __restrict__ union_off, int n, int
   int N = 64;
   while (N < m) N <<= 1;
   auto size_of = [&](int i) { return max(union_off[lo + i + 1] - union_off[lo + i], 0); };
-  if (N <= 1024) {
-    // key = (2^19 - 1 - min(size, 2^19 - 1)) << 13 | local index; padding sorts last
+  // (a range holding a union of 2^19 pages or more takes the 64-bit keys below)
+  if (N <= 1024 && !__syncthreads_or(t < m && size_of(t) > 0x7FFFF)) {
+    // key = (2^19 - 1 - size) << 13 | local index; padding sorts last
     uint32_t* k32 = reinterpret_cast<uint32_t*>(key);
     uint32_t v = 0xFFFFFFFFu;
-    if (t < m) v = ((uint32_t)(0x7FFFF - min(size_of(t), 0x7FFFF)) << 13) | (uint32_t)t;
+    if (t < m) v = ((uint32_t)(0x7FFFF - size_of(t)) << 13) | (uint32_t)t;
     for (int k = 2; k <= N; k <<= 1)
       for (int j = k >> 1; j > 0; j >>= 1) {
         uint32_t o;
@@ -657,10 +656,10 @@ __host__ __device__ constexpr int schedule_keys(int per) {
 __host__ __device__ constexpr int schedule_threads(int per) {
   return schedule_keys(per) < 1024 ? schedule_keys(per) : 1024;
 }
-// LDS for any range of m <= per items: 4 N(m) bytes up to 1024 keys, else 8 N(m) while
-// m <= kScheduleCap (a shorter last range may sort where the others keep item order)
+// LDS for any range of m <= per items: 8 N(m) bytes while m <= kScheduleCap (a shorter
+// last range may sort where the others keep item order)
 __host__ __device__ constexpr int schedule_lds_bytes(int per) {
-  return per <= 1024 ? 4 * schedule_keys(per) : 8 * schedule_keys(per < kScheduleCap ? per : kScheduleCap);
+  return 8 * schedule_keys(per < kScheduleCap ? per : kScheduleCap);
 }
 
 __global__ __launch_bounds__(1024) void k_schedule(const int32_t* __restrict__ union_off, int n,

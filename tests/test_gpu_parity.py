@@ -287,6 +287,22 @@ def test_work_order_matches_oracle(n):
     assert np.array_equal(order.cpu().numpy(), np.array(prep.work_order(sizes.tolist()), dtype=np.int32))
 
 
+@pytest.mark.parametrize("n", [100, 3000])
+def test_work_order_large_unions(n):
+    """Unions of 2^19 pages and more (past the one-key-per-thread form's size field) are
+    still ordered by their exact sizes."""
+    rng = np.random.default_rng(n + 1)
+    sizes = rng.integers(0, 1 << 21, size=n).astype(np.int64) if n <= 100 else \
+        np.where(rng.random(n) < 0.01, rng.integers(1 << 19, 1 << 20, size=n), rng.integers(0, 600, size=n))
+    sizes[:3] = [(1 << 19) + 5, (1 << 19) - 1, (1 << 19) + 5]   # ties across the boundary
+    off = np.zeros(n + 1, dtype=np.int64)
+    off[1:] = np.cumsum(sizes)
+    assert off[-1] < 2**31
+    order = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    pw.pw_schedule_items(torch.from_numpy(off.astype(np.int32)).cuda(), order)
+    assert np.array_equal(order.cpu().numpy(), np.array(prep.work_order(sizes.tolist()), dtype=np.int32))
+
+
 @pytest.mark.parametrize("nq,max_group", [(9, 8), (700, 1), (9000, 1), (65537, 1), (66000, 1)])
 def test_prepare_work_order(nq, max_group):
     """pw_prepare's work order (listed in the union listing's launch) equals pw_schedule_items
