@@ -97,12 +97,17 @@ struct Params {
 };
 
 // XOR swizzle of the 16-byte chunks of one LDS token row.  Chosen so that the K
-// operand reads (16 rows per quarter-wave, one chunk each) and the transposing V reads
-// (8 rows x 2 chunks per half-wave) fall on distinct banks.
+// operand reads and the transposing V reads fall on distinct banks.  Measured on gfx950
+// (64 banks of 4 bytes): a 16-byte read serves the wave in four phases of 16 lanes that
+// start at lane 8 (lanes 8..23, 24..39, 40..55, 56..63 with 0..7); an 8-byte transposing
+// read in two phases of 32 lanes.  For 256-byte rows (bf16, d = 128) a phase then holds
+// the K rows of two neighbouring row groups, and chunk bit 0 taken from key bit 2 (not
+// bit 4) keeps them apart: no bank conflicts on either read, against 4 conflict cycles
+// per K read before.
 template <int CHUNKS>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (CHUNKS >= 16) {
-    return (((r >> 4) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 3)) & (CHUNKS - 1);
+    return (((r >> 2) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 3)) & (CHUNKS - 1);
   } else {
     return (((r >> 1) & 1) | (((r >> 3) & 1) << 1) | ((((r >> 2) ^ (r >> 4)) & 1) << 2)) & (CHUNKS - 1);
   }
