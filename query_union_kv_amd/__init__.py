@@ -483,7 +483,8 @@ class SparsePrefill:
     arrange: bool = False       # topk mode: members arranged for row tiles (pw_arrange_groups)
     n_split: int = 0            # block_union mode: table slices per KV head (0: enough to
                                 # give every SIMD two waves; 1: no partials)
-    schedule: bool = True       # topk mode: start the largest unions first (pw_schedule_items)
+    schedule: bool = True       # topk mode: start the largest unions first (the work order of
+                                # pw_schedule_items; listed by pw_prepare when fused)
     device: str = "cuda"
 
     def __post_init__(self):
