@@ -326,6 +326,27 @@ def main():
                 "prep_ms": t_arr_prep, "attn_ms": t_arr_attn, "attn_ms_pick_order": t_fixed}
             del arr
 
+        # Wide groups (items of more than 32 rows, the two-wave form) run as two halves, each
+        # over the union of its own members' pages: the same outputs bit for bit.
+        if cfg.g * cfg.max_group > 32 and cfg.max_group % 2 == 0:
+            hv = pw.SparsePrefill(nq=cfg.nq, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, n_pages=cfg.n_pages,
+                                  page_size=cfg.ps, kv_len=cfg.kv_len, k=ids.shape[2], window=cfg.window,
+                                  max_group=cfg.max_group, halves=True, device=dev)
+            out_hv = torch.empty_like(q)
+            t_hv_prep = timed(lambda: hv.prepare(ids, stream))
+            for _ in range(30):   # (a form not run so far: settle it before timing)
+                hv.attend(q, kc, vc, q_pos, out_hv, ks, vs, stream=stream)
+            t_hv_attn = timed(lambda: hv.attend(q, kc, vc, q_pos, out_hv, ks, vs, stream=stream), n=30)
+            plan.attend(q, kc, vc, q_pos, out, ks, vs, stream=stream)   # whole groups, again
+            torch.cuda.synchronize()
+            extras["half_groups"] = {
+                "prep_ms": t_hv_prep, "attn_ms": t_hv_attn, "call_ms": t_hv_prep + t_hv_attn,
+                "queries_per_s": cfg.nq / ((t_hv_prep + t_hv_attn) / 1e3),
+                "union_pages": int(hv.union_off[-1].item()), "union_pages_whole_groups": total_pages,
+                "attn_ms_whole_groups": t_fixed,
+                "bit_identical": bool(torch.equal(out_hv.view(torch.int16), out.view(torch.int16)))}
+            del hv, out_hv
+
         # The direct KV-page union on the same inputs: every (KV head, page) once,
         # per-page partials, lse merge (a separate entry point, compared here).
         pu = pw.PageUnionPrefill(nq=cfg.nq, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, n_pages=cfg.n_pages,

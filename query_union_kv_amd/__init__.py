@@ -459,7 +459,11 @@ class SparsePrefill:
 
     Per-query mode (``topk`` given): page bitsets -> affinity grouping (or
     original-order groups when ``grouping='original'``) -> union tables with
-    member masks -> union attention.
+    member masks -> union attention.  With ``halves=True`` the groups are run as
+    two halves, each over the union of its own members' pages (a page both halves
+    selected is read twice): every row sees the same pages in the same order, so
+    the outputs are bit-identical, and wide groups (8 members x 8 query heads)
+    avoid the two-wave form, whose waves wait on each other's tiles.
     Block-union mode (``mask_rows`` given, CompactAttention's per-KV-group
     block table): bitsets of the mask rows -> one union over every row of a
     KV head -> attention of consecutive query groups over that shared table;
@@ -485,17 +489,21 @@ class SparsePrefill:
                                 # give every SIMD two waves; 1: no partials)
     schedule: bool = True       # topk mode: start the largest unions first (the work order of
                                 # pw_schedule_items; listed by pw_prepare when fused)
+    halves: bool = False        # topk mode: run each group as two halves of max_group / 2
+                                # members, each over the union of its own members' pages
     device: str = "cuda"
 
     def __post_init__(self):
         dev = self.device
         w = pw_words(self.n_pages)
         i32 = dict(dtype=torch.int32, device=dev)
+        if self.halves and (self.mode != "topk" or self.max_group % 2):
+            raise ValueError("halves needs topk mode and an even max_group")
         if self.mode == "topk":
             self.n_rows = self.nq
             self.n_groups = pw_num_groups(self.nq, self.window, self.max_group)
-            self.width = self.max_group
-            n_tables = self.hkv * self.n_groups
+            self.width = self.max_group // 2 if self.halves else self.max_group
+            n_tables = self.hkv * self.n_groups * (2 if self.halves else 1)
         elif self.mode == "block_union":
             self.n_groups = -(-self.nq // self.max_group)
             self.width = self.n_rows
@@ -512,6 +520,11 @@ class SparsePrefill:
             self.group_size = torch.empty((self.hkv, self.n_groups), **i32)
             self.union_qmask = torch.empty(max(cap, 1), dtype=torch.uint8, device=dev)
             self.item_order = torch.empty(n_tables, **i32) if self.schedule else None
+            if self.halves:
+                # half h of group j is the row [h * mg/2, (h + 1) * mg/2) of its member list (a
+                # view); absent members stay -1, so every half reports mg/2 members
+                self.half_qids = self.group_qids.view(self.hkv, 2 * self.n_groups, self.width)
+                self.half_size = torch.full((self.hkv, 2 * self.n_groups), self.width, **i32)
             if self.grouping == "original":
                 ids = torch.arange(self.n_groups * self.max_group, **i32).view(self.n_groups, self.max_group)
                 ids = torch.where(ids < self.nq, ids, torch.full_like(ids, -1))
@@ -532,6 +545,16 @@ class SparsePrefill:
 
     def prepare(self, ids: torch.Tensor, stream=None) -> None:
         """Bitsets, grouping and union tables from topk [nq, hkv, k] or mask rows [n_rows, hkv, k]."""
+        if self.halves:
+            pw_page_bitsets(ids, self.n_pages, self.bits, self.bad_ids, stream)
+            if self.grouping == "affinity":
+                pw_group(self.bits, self.n_pages, self.window, self.max_group, self.group_qids,
+                         self.group_size, stream)
+            pw_union_tables(self.bits, self.n_pages, self.half_qids, None, self.k, self.union_off,
+                            self.union_pages, self.union_qmask, stream)
+            if self.item_order is not None:
+                pw_schedule_items(self.union_off, self.item_order, stream)
+            return
         if self.mode == "topk" and self.grouping == "affinity" and self.fused:
             # (the work order comes with the tables; arranging members keeps union sizes)
             pw_prepare(ids, self.n_pages, self.window, self.max_group, self.bits, self.group_qids,
@@ -566,6 +589,13 @@ class SparsePrefill:
                                     partial_o=self.partial_o, partial_lse=self.partial_lse,
                                     k_scale=k_scale, v_scale=v_scale, sm_scale=sm_scale, lse=lse,
                                     stream=stream)
+            return
+        if self.halves:
+            pw_sparse_prefill(q, k_cache, v_cache, q_pos, kv_len, self.union_off, self.union_pages,
+                              out, hkv=self.hkv, n_groups=2 * self.n_groups, max_group=self.width,
+                              group_qids=self.half_qids, group_size=self.half_size,
+                              union_qmask=self.union_qmask, k_scale=k_scale, v_scale=v_scale,
+                              sm_scale=sm_scale, lse=lse, item_order=self.item_order, stream=stream)
             return
         pw_sparse_prefill(q, k_cache, v_cache, q_pos, kv_len, self.union_off, self.union_pages,
                           out, hkv=self.hkv, n_groups=self.n_groups, max_group=self.max_group,

@@ -174,6 +174,52 @@ def test_fused_prepare_equals_separate_steps(kw):
     _compare_tables(a, oracle_tables(w))
 
 
+HALF_SHAPES = [
+    dict(hq=16, hkv=2, nq=130, k=16, kv_len=4096, kv_dtype="fp8"),           # G = 8: 64-row groups
+    dict(hq=16, hkv=2, nq=77, k=8, kv_len=2048, kv_dtype="bf16"),            # ragged last window
+    dict(hq=8, hkv=2, nq=200, k=16, kv_len=8192, kv_dtype="fp8", window=32),  # G = 4
+]
+
+
+@pytest.mark.parametrize("kw", HALF_SHAPES, ids=["g8-fp8", "g8-bf16-ragged", "g4-fp8"])
+def test_half_groups_bit_identical(kw):
+    """Running every group as two halves over their own unions gives the outputs and lse of
+    the whole-group execution bit for bit, and both match the oracle."""
+    from gpu_util import make_plan
+    cfg = _small(**kw)
+    print(f"[parity] half groups {kw}", flush=True)
+    w = make_workload(cfg)
+    w.topk = add_padding_and_duplicates(w.topk, seed=cfg.seed + 3)
+    d = device_inputs(w)
+    res = []
+    for halves in (False, True):
+        base = make_plan(w)
+        plan = type(base)(**{**{f: getattr(base, f) for f in ("nq", "hq", "hkv", "d", "n_pages", "page_size",
+                                                               "kv_len", "k", "window", "max_group", "mode",
+                                                               "grouping", "n_rows", "fused")},
+                             "halves": halves})
+        out = torch.full_like(d["q"], float("nan"))
+        lse = torch.full(d["q"].shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+        plan(d["ids"], d["q"], d["k"], d["v"], d["q_pos"], out, d["k_scale"], d["v_scale"], lse)
+        torch.cuda.synchronize()
+        res.append((out.view(torch.int16).cpu(), lse.cpu(), plan))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+    # the halves' tables are the unions of each half's members
+    ref = oracle_tables(w)
+    assert np.array_equal(res[1][2].group_qids.cpu().numpy(), ref["group_qids"])
+    bits = prep.page_bitsets(w.topk, cfg.n_pages)
+    halves_per_head = [[h for m in grp for h in (m[:cfg.max_group // 2], m[cfg.max_group // 2:])]
+                       for grp in ref["groups"]]
+    off, pages, qmask = prep.union_tables(bits, halves_per_head)
+    plan = res[1][2]
+    assert np.array_equal(plan.union_off.cpu().numpy(), off)
+    assert np.array_equal(plan.union_pages[:len(pages)].cpu().numpy(), pages)
+    assert np.array_equal(plan.union_qmask[:len(qmask)].cpu().numpy(), qmask)
+    O, L = oracle_attention(w, ref["S"])
+    check_close(res[1][0].view(torch.bfloat16).float().numpy(), O, cfg.kv_dtype, "halves")
+    check_lse(res[1][1].numpy(), L, "halves")
+
+
 @pytest.mark.parametrize("n_split", [1, 2, 3, 7])
 def test_block_union_table_slices(n_split):
     """Shared per-KV-group tables cut into n_split slices (partials merged by lse) give the
