@@ -892,14 +892,20 @@ pw_status launch_nw(const Params& p, hipStream_t stream) {
   return launch_t<D, FP8, MT, NW, 4>(p, stream);
 }
 
-// Rows per work item: <= 16 -> one wave, one row tile; <= 32 -> one wave, two row tiles;
-// more -> 2, 4 or 8 waves of two row tiles sharing the LDS ring (the wide forms serve
-// shared per-KV-group tables, where every extra row reuses the staged tile).
+// Rows per work item: <= 16 -> one wave, one row tile; <= 32 -> one wave, two row tiles,
+// or two waves of one row tile where the one-wave form's ring leaves less than two waves
+// per SIMD (bf16, d = 128: 32 KiB per item, five items per CU); more -> 2, 4 or 8 waves
+// of two row tiles sharing the LDS ring (the wide forms serve shared per-KV-group tables,
+// where every extra row reuses the staged tile).  The two-wave form of a 32-row item
+// computes its two row tiles in parallel over the same staged tiles: on the 2K-query GQA
+// bf16 chunk 0.180 -> 0.152 ms; where LDS admits two one-wave items per SIMD (fp8) it is
+// slower (64K fp8 Top16: 0.313 -> 0.334 ms).  Outputs are identical either way.
 template <int D, bool FP8>
 pw_status launch_d(const Params& p, int rows, hipStream_t stream) {
   constexpr int kSlots = kTK * D * (FP8 ? 1 : 2) / 1024;    // 1 KiB load slots per tensor
+  constexpr bool kSplit32 = Cfg<D, FP8, 2, 1, 2>::kLdsWaves < 2;
   if (rows <= 16) return launch_nw<D, FP8, 1, 1>(p, stream);
-  if (rows <= 32) return launch_nw<D, FP8, 2, 1>(p, stream);
+  if (rows <= 32) return kSplit32 ? launch_nw<D, FP8, 1, 2>(p, stream) : launch_nw<D, FP8, 2, 1>(p, stream);
   if (rows <= 64) return launch_nw<D, FP8, 2, 2>(p, stream);
   if constexpr (kSlots >= 4) if (rows <= 128) return launch_nw<D, FP8, 2, 4>(p, stream);
   if constexpr (kSlots >= 8) if (rows <= 256) return launch_nw<D, FP8, 2, 8>(p, stream);
