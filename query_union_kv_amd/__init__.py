@@ -499,6 +499,8 @@ class SparsePrefill:
         i32 = dict(dtype=torch.int32, device=dev)
         if self.halves and (self.mode != "topk" or self.max_group % 2):
             raise ValueError("halves needs topk mode and an even max_group")
+        if self.halves and self.arrange:
+            raise ValueError("halves and arrange are not combined")
         if self.mode == "topk":
             self.n_rows = self.nq
             self.n_groups = pw_num_groups(self.nq, self.window, self.max_group)

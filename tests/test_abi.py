@@ -273,3 +273,15 @@ def test_arrange_validation(args, code):
 def test_arrange_is_a_noop_where_tiles_leave_no_choice():
     assert L.pw_arrange_groups(NULL, 64, 2, 16, 16, 8, 8, NULL, NULL, NULL, NULL, 0, NULL) == 0  # G = 8
     assert L.pw_arrange_groups(NULL, 64, 2, 16, 8, 16, 4, NULL, NULL, NULL, NULL, 0, NULL) == 0  # 4 members
+
+
+def test_sparse_prefill_rejects_bad_half_groups():
+    """halves=True needs per-query mode, an even group size and no member arrangement
+    (checked before any device memory is touched)."""
+    kw = dict(nq=64, hq=8, hkv=2, d=128, n_pages=16, page_size=64, kv_len=1024, k=4, device="cpu")
+    with pytest.raises(ValueError):
+        pw.SparsePrefill(max_group=7, halves=True, **kw)
+    with pytest.raises(ValueError):
+        pw.SparsePrefill(max_group=8, halves=True, arrange=True, **kw)
+    with pytest.raises(ValueError):
+        pw.SparsePrefill(max_group=8, halves=True, mode="block_union", n_rows=8, **kw)
