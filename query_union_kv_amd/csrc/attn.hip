@@ -812,10 +812,32 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     if (t + ST - 1 < n_tiles) issue(t + ST - 1, std::integral_constant<int, (SS + ST - 1) % ST>{}, pg_next);
     compute(t, stage_c, pc);
   };
+  // Several waves over a four-stage ring step by pairs of tiles: tiles t, t + 1 have landed
+  // for every wave and every wave is done with t - 2, t - 1, whose stages then take t + 2 and
+  // t + 3.  One barrier per two tiles instead of one per tile, two tiles of prefetch instead
+  // of three (the 128K block-union chunk: 0.744 -> 0.731 ms).
+  constexpr bool kPairs = ST == 4 && NW > 1;
+  auto pair = [&](int t, auto sa, auto sb, auto sc, auto sd) {
+    wait_vmcnt<0>();                   // this wave's loads of t, t + 1 (nothing newer yet)
+    __builtin_amdgcn_s_barrier();      // ... and every other wave's
+    if (t + 2 < n_tiles) issue(t + 2, sc, kNoPage);
+    if (t + 3 < n_tiles) issue(t + 3, sd, kNoPage);
+    compute(t, sa, page_ctx(t));
+    if (t + 1 < n_tiles) compute(t + 1, sb, page_ctx(t + 1));
+  };
   if (0 < n_tiles) issue(0, std::integral_constant<int, 0>{}, kNoPage);
   if constexpr (ST > 2) if (1 < n_tiles) issue(1, std::integral_constant<int, 1>{}, kNoPage);
-  if constexpr (ST > 3) if (2 < n_tiles) issue(2, std::integral_constant<int, 2>{}, kNoPage);
-  if constexpr (ST == 2) {
+  if constexpr (ST > 3 && !kPairs) if (2 < n_tiles) issue(2, std::integral_constant<int, 2>{}, kNoPage);
+  if constexpr (kPairs) {
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    for (int t0 = 0; t0 < n_tiles; t0 += 4) {
+      pair(t0, S0{}, S1{}, S2{}, S3{});
+      if (t0 + 2 < n_tiles) pair(t0 + 2, S2{}, S3{}, S0{}, S1{});
+    }
+  } else if constexpr (ST == 2) {
     // a page holds 2 or 4 tiles and t0 is even, so tiles t0 and t0 + 1 share a page: its
     // values are read once, and the load of tile t0 + 1 needs no page lookup
     for (int t0 = 0; t0 < n_tiles; t0 += 2) {
