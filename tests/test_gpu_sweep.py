@@ -18,10 +18,11 @@ from workloads import make_workload
 from workloads.configs import Config
 
 N_CASES = 60
+N_LONG = 20   # contexts up to 140K tokens (past 1024 pages: the unfused preparation), windows up to 256
 
 
-def _case(i):
-    rng = random.Random(1000 + i)
+def _case(i, long=False):
+    rng = random.Random((5000 if long else 1000) + i)
     d = rng.choice([64, 128])
     kvd = rng.choice(["bf16", "fp8"])
     hkv = rng.choice([1, 2, 3])
@@ -30,10 +31,10 @@ def _case(i):
     while G * mg > 64:
         mg -= 1
     ps = rng.choice([64, 128])
-    kv_len = rng.choice([ps, 2 * ps + 5, 1000, 3000, 5000])
+    kv_len = rng.choice([70000, 140000] if long else [ps, 2 * ps + 5, 1000, 3000, 5000])
     nq = rng.randint(1, min(kv_len, 300))
     k = rng.randint(1, min(24, -(-kv_len // ps) + 2))
-    window = mg * rng.randint(1, max(1, 64 // mg))
+    window = mg * rng.randint(1, max(1, (256 if long else 64) // mg))
     halves = mg % 2 == 0 and rng.random() < 0.3
     cfg = Config(name=f"sweep{i}", hq=hkv * G, hkv=hkv, d=d, ps=ps, kv_len=kv_len, nq=nq, kv_dtype=kvd,
                  support="uniform", k=k, forced=rng.random() < 0.5, window=window, max_group=mg,
@@ -42,9 +43,9 @@ def _case(i):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("i", range(N_CASES))
-def test_random_shape(i):
-    cfg, halves, pad = _case(i)
+@pytest.mark.parametrize("i,long", [(i, False) for i in range(N_CASES)] + [(i, True) for i in range(N_LONG)])
+def test_random_shape(i, long):
+    cfg, halves, pad = _case(i, long)
     print(f"[sweep] case {i}: {cfg} halves={halves} pad={pad}", flush=True)
     w = make_workload(cfg)
     if pad:
