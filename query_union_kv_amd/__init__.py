@@ -687,16 +687,20 @@ class ChunkedPrefill:
 def sparse_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, topk: torch.Tensor,
                    q_pos: torch.Tensor, *, kv_len: int, k_scale: Optional[torch.Tensor] = None,
                    v_scale: Optional[torch.Tensor] = None, window: int = 64, max_group: int = 8,
-                   sm_scale: Optional[float] = None, with_lse: bool = False, stream=None):
+                   sm_scale: Optional[float] = None, with_lse: bool = False, halves: bool = False,
+                   stream=None):
     """One complete query-union call on the current stream: bitsets, affinity grouping and
     union tables from topk [nq, hkv, K], then attention.  q bf16 [nq, hq, d]; caches
     [hkv, n_pages, page_size, d] (bf16, or uint8 e4m3fn codes with fp32 scales
-    [hkv, n_pages]).  Returns (out, aux): out bf16 [nq, hq, d]; aux holds the plan with
-    its bitsets, groups and union tables, and lse [nq, hq] when with_lse."""
+    [hkv, n_pages]).  ``halves`` runs every group as two halves over their own unions
+    (the same outputs; see SparsePrefill).  Returns (out, aux): out bf16 [nq, hq, d]; aux
+    holds the plan with its bitsets, groups and union tables, and lse [nq, hq] when
+    with_lse."""
     nq, hq, d = q.shape
     hkv, n_pages, page_size, _ = k_cache.shape
     plan = SparsePrefill(nq=nq, hq=hq, hkv=hkv, d=d, n_pages=n_pages, page_size=page_size, kv_len=kv_len,
-                         k=topk.shape[2], window=window, max_group=max_group, device=q.device)
+                         k=topk.shape[2], window=window, max_group=max_group, halves=halves,
+                         device=q.device)
     out = torch.empty_like(q)
     lse = torch.empty((nq, hq), dtype=torch.float32, device=q.device) if with_lse else None
     plan.prepare(topk, stream)
