@@ -71,6 +71,83 @@ def route_a(q_bits, k_data, v_data, k_scale, v_scale, kv_dtype: str,
     return O, L
 
 
+def _route_a_batch(Kg, Vg, g, G, q_bits, S, q_pos, kv_len, ps, sm_scale, ids):
+    """Route A for the queries `ids` and the query heads of KV head g (its decoded K and V
+    given): returns O [len(ids), G, d] and lse [len(ids), G]."""
+    d = q_bits.shape[2]
+    sets = [S[g][i] for i in ids]
+    qh = bf16_bits_to_f64(q_bits[ids, g * G:(g + 1) * G])                  # [B, G, d]
+    pos = np.asarray([int(q_pos[i]) for i in ids], dtype=np.int64)
+    if sets[0] and all(s == sets[0] for s in sets):
+        # one support for the whole batch (a per-KV-group table): gathered once
+        pages = np.asarray(sorted(sets[0]), dtype=np.int64)[None, :]
+    else:
+        width = max(1, max(len(s) for s in sets))
+        pages = np.full((len(ids), width), -1, dtype=np.int64)              # -1: padding
+        for n, s in enumerate(sets):
+            pages[n, :len(s)] = sorted(s)
+    t = pages[:, :, None] * ps + np.arange(ps)[None, None, :]              # token of each slot
+    keep = (pages[:, :, None] >= 0) & (t <= pos[:, None, None]) & (t < kv_len)
+    keep = np.broadcast_to(keep.reshape(keep.shape[0], -1), (len(ids), t[0].size))
+    safe = np.maximum(pages, 0)
+    kk = Kg[safe].reshape(pages.shape[0], -1, d)                             # [1 or B, n, d]
+    vv = Vg[safe].reshape(pages.shape[0], -1, d)
+    s_t = sm_scale * np.matmul(qh, kk.transpose(0, 2, 1))                   # [B, G, n]
+    s_t = np.where(keep[:, None, :], s_t, -np.inf)                          # keys outside J(i, g)
+    has = keep.any(axis=1)
+    m = np.where(has[:, None, None], s_t.max(axis=2, keepdims=True), 0.0)
+    e = np.exp(s_t - m)                                                     # 0 outside J
+    l = e.sum(axis=2, keepdims=True)
+    o = np.matmul(e, vv) / np.where(has[:, None, None], l, 1.0)
+    O = np.where(has[:, None, None], o, 0.0)
+    L = np.where(has[:, None], (m + np.log(np.where(has[:, None, None], l, 1.0)))[:, :, 0], -np.inf)
+    return O, L
+
+
+def route_a_batched(q_bits, k_data, v_data, k_scale, v_scale, kv_dtype: str,
+                    S: List[List[frozenset]], q_pos, kv_len: int, ps: int, sm_scale: float,
+                    queries: Optional[Sequence[int]] = None, batch: int = 64, workers: int = 1):
+    """Route A (the definition) with `batch` queries per numpy call, the (KV head, batch)
+    pieces spread over `workers` threads.  Each query's scores, softmax and PV still use
+    its own keys J(i, g) only: its gathered support slots outside J (padding of a shorter
+    support, keys after its position or past the cache end) are excluded by an explicit
+    mask.  A batch whose queries share one support gathers it once (the per-KV-group block
+    table of CompactAttention's "Approach").  Same outputs as ``route_a`` (up to rounding
+    order); sized for whole chunks."""
+    nq, hq, d = q_bits.shape
+    hkv = k_data.shape[0]
+    G = hq // hkv
+    queries = list(range(nq)) if queries is None else list(queries)
+    O = np.zeros((len(queries), hq, d))
+    L = np.full((len(queries), hq), -np.inf)
+
+    def decode(g):
+        return (decode_kv(k_data[g], None if k_scale is None else k_scale[g], kv_dtype),
+                decode_kv(v_data[g], None if v_scale is None else v_scale[g], kv_dtype))
+
+    def piece(task):
+        g, b0 = task
+        Kg, Vg = heads[g]
+        o, l = _route_a_batch(Kg, Vg, g, G, q_bits, S, q_pos, kv_len, ps, sm_scale,
+                              queries[b0:b0 + batch])
+        O[b0:b0 + batch, g * G:(g + 1) * G] = o
+        L[b0:b0 + batch, g * G:(g + 1) * G] = l
+
+    tasks = [(g, b0) for g in range(hkv) for b0 in range(0, len(queries), batch)]
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as ex:
+            heads = list(ex.map(decode, range(hkv)))
+            list(ex.map(piece, tasks))
+    else:
+        heads = [decode(g) for g in range(hkv)]
+        for task in tasks:
+            piece(task)
+    return O, L
+
+
 def route_b(q_bits, k_data, v_data, k_scale, v_scale, kv_dtype: str,
             S: List[List[frozenset]], groups_per_g: List[List[List[int]]], q_pos,
             kv_len: int, ps: int, sm_scale: float):

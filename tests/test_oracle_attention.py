@@ -201,3 +201,53 @@ def test_direct_page_union_route_c_equals_definition(kv_dtype):
     fin = np.isfinite(LA)
     assert np.allclose(LC[fin], LA[fin], rtol=0, atol=1e-12)
     assert np.isneginf(LC[0, :2]).all() and not OC[0, :2].any()
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("batch,workers", [(1, 1), (5, 2), (64, 3)])
+def test_route_a_batched_equals_route_a(kv_dtype, batch, workers):
+    """The batched route A (padded gathers with an explicit J(i, g) mask, threads over KV
+    heads) gives route A's result: supports of different sizes with padding slots and
+    duplicates, an empty support, a page wholly after its query, positions past the
+    cache end and a cache end inside a page."""
+    w = tiny_workload(kv_dtype=kv_dtype, hq=6, hkv=3, d=16, ps=8, kv_len=197, nq=41, k=5, seed=15)
+    c = w.cfg
+    topk = add_padding_and_duplicates(w.topk, 4)
+    topk[0, 0, :] = -1                                        # an empty support
+    topk[1, 1, :2] = -1                                       # a shorter support
+    topk[2, 2, 0] = c.n_pages - 1                             # a page after the query
+    w.q_pos = w.q_pos.copy()
+    w.q_pos[-3:] += 9                                         # positions past the cache end
+    S = prep.supports(topk, c.n_pages)
+    OA, LA = _route_a(w, S)
+    OB, LB = attention.route_a_batched(w.q, w.k, w.v, w.k_scale, w.v_scale, kv_dtype, S, w.q_pos,
+                                       c.kv_len, c.ps, 1.0 / math.sqrt(c.d), batch=batch,
+                                       workers=workers)
+    assert np.allclose(OB, OA, rtol=0, atol=1e-12)
+    assert (np.isneginf(LB) == np.isneginf(LA)).all()
+    fin = np.isfinite(LA)
+    assert np.allclose(LB[fin], LA[fin], rtol=0, atol=1e-12)
+    assert not OB[0, :2].any() and np.isneginf(LB[0, :2]).all()
+    sel = [40, 3, 0, 17]
+    Os, Ls = attention.route_a_batched(w.q, w.k, w.v, w.k_scale, w.v_scale, kv_dtype, S, w.q_pos,
+                                       c.kv_len, c.ps, 1.0 / math.sqrt(c.d), queries=sel, batch=batch)
+    assert np.allclose(Os, OA[sel], rtol=0, atol=1e-12)
+
+
+def test_route_a_batched_shared_table_equals_route_a():
+    """A batch whose queries share one support (a per-KV-group block table) is gathered
+    once and still masked per query: the same result as route A, also against the
+    dense library attention when the table holds every page."""
+    w = tiny_workload(kv_dtype="bf16", hq=4, hkv=2, d=16, ps=8, kv_len=150, nq=30, seed=16)
+    c = w.cfg
+    tables = [[0, 3, 5, 6, 7, 9, 12, 15, 17, 18], [1, 2, 4, 8, 11, 16, 18]]
+    S = attention.shared_supports(tables, c.nq)
+    OA, LA = _route_a(w, S)
+    OB, LB = attention.route_a_batched(w.q, w.k, w.v, w.k_scale, w.v_scale, "bf16", S, w.q_pos,
+                                       c.kv_len, c.ps, 1.0 / math.sqrt(c.d), batch=8, workers=2)
+    assert np.allclose(OB, OA, rtol=0, atol=1e-12)
+    assert np.allclose(LB[np.isfinite(LA)], LA[np.isfinite(LA)], rtol=0, atol=1e-12)
+    Sd = attention.dense_supports(c.nq, c.hkv, c.n_pages)
+    Od, _ = attention.route_a_batched(w.q, w.k, w.v, None, None, "bf16", Sd, w.q_pos, c.kv_len, c.ps,
+                                      1.0 / math.sqrt(c.d), batch=7)
+    assert np.allclose(Od, _sdpa_dense(w), rtol=0, atol=1e-12)

@@ -57,6 +57,17 @@ MUTATIONS = [
      lambda: A.test_direct_page_union_route_c_equals_definition("bf16")),
     (attention, "route_c", "keep = (t <= int(q_pos[i])) & (t < kv_len)", "keep = (t < kv_len)",
      lambda: A.test_direct_page_union_route_c_equals_definition("fp8")),
+    (attention, "_route_a_batch", "(t <= pos[:, None, None])", "(t < pos[:, None, None])",
+     lambda: A.test_route_a_batched_equals_route_a("bf16", 5, 2)),
+    (attention, "_route_a_batch", "(pages[:, :, None] >= 0) & ", "",
+     lambda: A.test_route_a_batched_equals_route_a("fp8", 64, 3)),
+    (attention, "_route_a_batch", "q_bits[ids, g * G:(g + 1) * G]", "q_bits[ids, g:g + G]",
+     lambda: A.test_route_a_batched_equals_route_a("bf16", 1, 1)),
+    (attention, "_route_a_batch", "& (t < kv_len)", "& (t <= kv_len)",
+     lambda: A.test_route_a_batched_equals_route_a("bf16", 64, 3)),
+    (attention, "_route_a_batch", "pages = np.asarray(sorted(sets[0]), dtype=np.int64)[None, :]",
+     "pages = np.asarray(sorted(sets[0]), dtype=np.int64)[None, 1:]",
+     lambda: A.test_route_a_batched_shared_table_equals_route_a()),
     (prep, "page_items", "support_rank(bits_g[q], p)", "support_rank(bits_g[q], p + 1)",
      lambda: P.test_page_items_hand_trace()),
     (prep, "page_items", "range(0, len(qs), chunk)", "range(0, len(qs), chunk + 1)",
