@@ -737,13 +737,25 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
         scores(bias0, pv, std::false_type{});
       else
         scores(bias0, pv, std::true_type{});
-      // this lane's share of the row sum (its 8 of the tile's 32 keys); the four lanes of a
-      // row are added up once, in the epilogue
-      // (summed as a tree: three dependent adds instead of eight)
-      auto sum8 = [](const float* x) { return ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7])); };
+      // P is rounded to bf16 for the PV MFMA, and the row sum adds up exactly those rounded
+      // values: numerator and denominator then carry the same weights, so a row whose
+      // softmax is dominated by one key gets that key's value without the rounding of its
+      // weight (which would otherwise reach 2^-9 of |V|).  This lane's share of the row
+      // sum (its 8 of the tile's 32 keys) comes from four bf16 dot products with ones; the
+      // four lanes of a row are added up once, in the epilogue.
+      auto round_sum = [&](const float* x, bf16x8& pb) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) pb[k] = (__bf16)x[k];
+        const bf16x2 one{(__bf16)1.0f, (__bf16)1.0f};
+        float s01 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[0], pb[1]}, one, 0.f, false);
+        float s45 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[4], pb[5]}, one, 0.f, false);
+        s01 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[2], pb[3]}, one, s01, false);
+        s45 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[6], pb[7]}, one, s45, false);
+        return s01 + s45;
+      };
 #pragma unroll
       for (int k = 0; k < 8; ++k) pv[k] = __builtin_amdgcn_exp2f(pv[k]);
-      float lsum = sum8(pv);
+      float lsum = round_sum(pv, pf[m]);
       // The reference must be set (first used tile of a row) or raised (a lane's share of a
       // row sum passed 2^30, or overflowed): rare, wave-uniform slow path.  The decision is
       // made per row - lanes li, li+16, li+32 and li+48 hold row li - so that every key of
@@ -773,11 +785,9 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
           const float bias = (sel && m_new != -INFINITY) ? lvs - m_new : -INFINITY;
 #pragma unroll
           for (int k = 0; k < 8; ++k) pv[k] = __builtin_amdgcn_exp2f(raw[k] + bias);
-          lsum = sum8(pv);
+          lsum = round_sum(pv, pf[m]);
         }
       }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) pf[m][k] = (__bf16)pv[k];
       l_run[m] += lsum * inv_vs;
     }
 

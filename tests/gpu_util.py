@@ -1,6 +1,7 @@
 """Shared pieces of the GPU parity tests: moving a workload to the device, running
 the HIP path through the C ABI, and the oracle's view of the same call."""
 import math
+import os
 
 import numpy as np
 import torch
@@ -57,6 +58,7 @@ def run_gpu(w, grouping="affinity", window=None, max_group=None, with_lse=True, 
     res["union_pages"] = plan.union_pages[:total].cpu().numpy()
     if plan.union_qmask is not None:
         res["union_qmask"] = plan.union_qmask[:total].cpu().numpy()
+    if plan.group_qids is not None:
         res["group_qids"] = plan.group_qids.cpu().numpy()
         res["group_size"] = plan.group_size.cpu().numpy()
     if getattr(plan, "item_order", None) is not None:
@@ -93,10 +95,18 @@ def oracle_tables(w, grouping="affinity", window=None, max_group=None, arrange=F
             "tables": tables, "S": attention.shared_supports(tables, c.nq)}
 
 
+def oracle_workers() -> int:
+    """Threads for the oracle: the cores this process may run on, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def oracle_attention(w, S, queries=None):
+    """Route A (the definition) for every row, or for ``queries``; batched over queries
+    and threaded over KV heads so that whole chunks take seconds."""
     c = w.cfg
-    return attention.route_a(w.q, w.k, w.v, w.k_scale, w.v_scale, c.kv_dtype, S, w.q_pos,
-                             c.kv_len, c.ps, 1.0 / math.sqrt(c.d), queries)
+    return attention.route_a_batched(w.q, w.k, w.v, w.k_scale, w.v_scale, c.kv_dtype, S, w.q_pos,
+                                     c.kv_len, c.ps, 1.0 / math.sqrt(c.d), queries,
+                                     workers=oracle_workers())
 
 
 def check_close(got, ref, kv_dtype, what=""):
@@ -109,7 +119,14 @@ def check_close(got, ref, kv_dtype, what=""):
     return float(err.max()), float(err.mean()), attention.nrms(got, ref)
 
 
+# lse is not given a tolerance by the task; this one follows from the arithmetic: the
+# kernel's row sum adds the bf16-rounded probabilities that its PV products use (each within
+# 2^-9 relative), so ln(l) may be off by ln(1 + 2^-9) = 1.95e-3, on top of the fp32 score
+# error (and, for fp8 K, the split of each query row into two e4m3 parts)
+LSE_TOL = 4e-3
+
+
 def check_lse(got, ref, what=""):
     fin = np.isfinite(ref)
     assert (np.isneginf(got) == ~fin).all(), f"{what}: lse -inf pattern differs"
-    assert np.abs(got[fin] - ref[fin]).max(initial=0) <= 2e-3, f"{what}: lse differs"
+    assert np.abs(got[fin] - ref[fin]).max(initial=0) <= LSE_TOL, f"{what}: lse differs"
