@@ -160,7 +160,10 @@ pw_status pw_arrange_groups(const uint64_t* bits, int nq, int hkv, int n_pages, 
  *
  * bits         uint64 [hkv][n_rows][pw_words(n_pages)]
  * group_rows   int32 [hkv][n_groups][group_width]: row indices (-1 padded); member j
- *              of a table is group_rows[..][j]
+ *              of a table is group_rows[..][j].  NULL: consecutive groups, member j of
+ *              table g * n_groups + i is row i * group_width + j (rows >= n_rows absent),
+ *              the original-order groups of PageWeaver Fig. 2 (then n_groups * group_width
+ *              >= n_rows is required)
  * group_size   int32 [hkv][n_groups] or NULL (then every table has group_width members)
  * union_off    int32 [hkv*n_groups + 1] output: exclusive prefix sum of union sizes
  * union_pages  int32 [capacity] output: pages of table e at [union_off[e], union_off[e+1])
@@ -231,6 +234,14 @@ pw_status pw_prepare(const int32_t* topk, int nq, int hkv, int k, int n_pages, i
  * out         bf16 [nq][hq][d]; each row written exactly once if it belongs to
  *             a group; rows of queries in no group are left untouched
  * lse         fp32 [nq][hq] or NULL
+ * Precondition on the cache contents: every K and V slot of every page in a work
+ * item's table - the slots at and past kv_len included - holds a finite value, with
+ * scaled scores inside the fp32 range.  Keys a row does not use get probability 0,
+ * but they still pass through the MFMAs of its 16-row tile, so a NaN or infinity
+ * there (in a page only another member selected, or past the cache end) would reach
+ * rows whose result does not depend on it; with finite contents such slots change no
+ * bit of those rows.  pw_append_kv writes zeros into the slots after a chunk's last
+ * token, so a cache filled by it meets the precondition.
  * Limits: d in {64, 128}; page_size in {64, 128}; hq % hkv == 0; 1 <= n_pages <= 2^24 - 2;
  *   with group_qids or union_qmask: 1 <= max_group <= 8 and G * max_group <= 64;
  *   with neither (consecutive groups, every member uses every page of its table -

@@ -205,13 +205,17 @@ def pw_arrange_groups(bits: torch.Tensor, n_pages: int, hq: int, group_qids: tor
                                    union_qmask.numel() if union_qmask is not None else 0, _stream(stream)))
 
 
-def pw_union_tables(bits: torch.Tensor, n_pages: int, group_rows: torch.Tensor,
+def pw_union_tables(bits: torch.Tensor, n_pages: int, group_rows: Optional[torch.Tensor],
                     group_size: Optional[torch.Tensor], k_max: int, union_off: torch.Tensor,
                     union_pages: torch.Tensor, union_qmask: Optional[torch.Tensor] = None,
-                    stream=None) -> None:
-    """bits [hkv, n_rows, words], group_rows int32 [hkv, n_groups, width] -> CSR union tables."""
+                    stream=None, *, n_groups: Optional[int] = None, width: Optional[int] = None) -> None:
+    """bits [hkv, n_rows, words], group_rows int32 [hkv, n_groups, width] -> CSR union tables.
+    group_rows None: consecutive groups of ``width`` rows (``n_groups`` of them per KV head)."""
     hkv, n_rows, _ = bits.shape
-    _, n_groups, width = group_rows.shape
+    if group_rows is not None:
+        _, n_groups, width = group_rows.shape
+    elif n_groups is None or width is None:
+        raise ValueError("consecutive groups (group_rows=None) need n_groups and width")
     if union_off.numel() != hkv * n_groups + 1:
         raise ValueError("union_off must have hkv*n_groups+1 entries")
     if union_qmask is not None and union_qmask.numel() < union_pages.numel():
@@ -528,10 +532,13 @@ class SparsePrefill:
                 self.half_qids = self.group_qids.view(self.hkv, 2 * self.n_groups, self.width)
                 self.half_size = torch.full((self.hkv, 2 * self.n_groups), self.width, **i32)
             if self.grouping == "original":
-                ids = torch.arange(self.n_groups * self.max_group, **i32).view(self.n_groups, self.max_group)
-                ids = torch.where(ids < self.nq, ids, torch.full_like(ids, -1))
-                self.group_qids.copy_(ids.expand(self.hkv, -1, -1))
-                self.group_size.copy_((ids >= 0).sum(1, dtype=torch.int32).expand(self.hkv, -1))
+                # consecutive groups: the library lists their unions and runs them from
+                # their ranks alone (group_rows / group_qids NULL), no member lists
+                if self.halves or self.arrange:
+                    raise ValueError("original-order groups take neither halves nor arrange")
+                if -(-self.nq // self.max_group) != self.n_groups:
+                    raise ValueError("original-order groups need window % max_group == 0")
+                self.group_qids = self.group_size = None
         else:
             self.group_rows = torch.arange(self.n_rows, **i32).view(1, 1, -1).repeat(self.hkv, 1, 1)
             self.group_qids = self.group_size = self.union_qmask = self.item_order = None
@@ -572,7 +579,8 @@ class SparsePrefill:
                 pw_group(self.bits, self.n_pages, self.window, self.max_group, self.group_qids,
                          self.group_size, stream)
             pw_union_tables(self.bits, self.n_pages, self.group_qids, self.group_size, self.k,
-                            self.union_off, self.union_pages, self.union_qmask, stream)
+                            self.union_off, self.union_pages, self.union_qmask, stream,
+                            n_groups=self.n_groups, width=self.max_group)
             if self.arrange:
                 pw_arrange_groups(self.bits, self.n_pages, self.hq, self.group_qids, self.group_size,
                                   self.union_off, self.union_qmask, stream)

@@ -179,7 +179,9 @@ pw_status pw_union_tables(const uint64_t* bits, int n_rows, int hkv, int n_pages
     return fail(PW_ERR_UNSUPPORTED, "pw_union_tables: capacity %lld exceeds int32 offsets",
                 (long long)capacity);
   if (!union_off) return fail(PW_ERR_ARG, "pw_union_tables: null union_off");
-  if (n_tables > 0 && (!bits || !group_rows || (need > 0 && !union_pages)))
+  if (group_rows == nullptr && (int64_t)n_groups * group_width < n_rows)
+    return fail(PW_ERR_ARG, "pw_union_tables: consecutive groups need n_groups*group_width >= n_rows");
+  if (n_tables > 0 && (!bits || (need > 0 && !union_pages)))
     return fail(PW_ERR_ARG, "pw_union_tables: null pointer argument");
   return pw::launch_union_tables(bits, n_rows, hkv, n_pages, group_rows, group_size, n_groups,
                                  group_width, union_off, union_pages, union_qmask, capacity,

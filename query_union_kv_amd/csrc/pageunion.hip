@@ -209,21 +209,20 @@ __global__ __launch_bounds__(64) void k_page_merge(
   const int hq = hkv * G;
   for (int i = lane; i < n * G; i += kWave) wts[i] = part_lse[slot0 * G + i];
   __syncthreads();
-  float row_lse = -INFINITY;
-  if (lane < G) {
+  // each lane owns head columns h = lane, lane + 64, ... of the weights: their lse, then
+  // their weights in place (no other lane touches them)
+  for (int h = lane; h < G; h += kWave) {
+    float row_lse = -INFINITY;
     float m = -INFINITY;
-    for (int r = 0; r < n; ++r) m = fmaxf(m, wts[r * G + lane]);
+    for (int r = 0; r < n; ++r) m = fmaxf(m, wts[r * G + h]);
     if (m != -INFINITY) {
       float s = 0.f;
-      for (int r = 0; r < n; ++r) s += __expf(wts[r * G + lane] - m);
+      for (int r = 0; r < n; ++r) s += __expf(wts[r * G + h] - m);
       row_lse = m + __logf(s);
     }
-  }
-  __syncthreads();
-  if (lane < G) {
     for (int r = 0; r < n; ++r)
-      wts[r * G + lane] = row_lse == -INFINITY ? 0.f : __expf(wts[r * G + lane] - row_lse);
-    if (lse) lse[(int64_t)q * hq + g * G + lane] = row_lse;
+      wts[r * G + h] = row_lse == -INFINITY ? 0.f : __expf(wts[r * G + h] - row_lse);
+    if (lse) lse[(int64_t)q * hq + g * G + h] = row_lse;
   }
   __syncthreads();
   constexpr int kC = D / 8;   // 8-element chunks per head row

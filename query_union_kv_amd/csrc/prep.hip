@@ -523,6 +523,13 @@ __device__ __forceinline__ int member_count(const int32_t* group_size, int e, in
   return group_size ? min(max(group_size[e], 0), group_width) : group_width;
 }
 
+// Row of member j of table e: group_rows[e][j], or with group_rows NULL the consecutive
+// rows of the KV head's group e % n_groups, (e % n_groups) * group_width + j.
+__device__ __forceinline__ int member_row(const int32_t* group_rows, int e, int n_groups,
+                                          int group_width, int j) {
+  return group_rows ? group_rows[(int64_t)e * group_width + j] : (e % n_groups) * group_width + j;
+}
+
 __global__ void k_union_count(const uint64_t* __restrict__ bits, int n_rows, int words,
                               const int32_t* __restrict__ group_rows,
                               const int32_t* __restrict__ group_size, int n_groups, int n_tables,
@@ -532,12 +539,11 @@ __global__ void k_union_count(const uint64_t* __restrict__ bits, int n_rows, int
   if (e >= n_tables) return;
   const int g = e / n_groups;
   const int sz = member_count(group_size, e, group_width);
-  const int32_t* rows = group_rows + (int64_t)e * group_width;
   int cnt = 0;
   for (int w = lane; w < words; w += kWave) {
     uint64_t u = 0;
     for (int j = 0; j < sz; ++j) {
-      const int r = rows[j];
+      const int r = member_row(group_rows, e, n_groups, group_width, j);
       if (r >= 0 && r < n_rows) u |= bits[((int64_t)g * n_rows + r) * words + w];
     }
     cnt += __popcll(u);
@@ -683,11 +689,10 @@ __device__ void emit_table(const uint64_t* __restrict__ bits, int n_rows, int wo
   if (e >= n_tables) return;
   const int g = e / n_groups;
   const int sz = member_count(group_size, e, group_width);
-  const int32_t* rows = group_rows + (int64_t)e * group_width;
   int r[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    r[j] = j < sz ? rows[j] : -1;
+    r[j] = j < sz ? member_row(group_rows, e, n_groups, group_width, j) : -1;
     if (r[j] >= n_rows) r[j] = -1;   // (negative: no member)
   }
   const int sh = 16 * (lane & 3);
@@ -705,7 +710,7 @@ __device__ void emit_table(const uint64_t* __restrict__ bits, int n_rows, int wo
     }
     if (!QMASK)   // (member masks need at most 8 members; plain tables take up to 64)
       for (int j = 8; j < sz; ++j) {
-        const int rj = rows[j];
+        const int rj = member_row(group_rows, e, n_groups, group_width, j);
         if (w < words && rj >= 0 && rj < n_rows)
           u |= (uint32_t)(bits[((int64_t)g * n_rows + rj) * words + w] >> sh) & 0xFFFFu;
       }
