@@ -52,12 +52,6 @@ def compare_items(res, ref):
         assert np.array_equal(res[k], ref[k]), f"{k} differs"
 
 
-def _sample(nq, n=40, seed=0):
-    rng = np.random.default_rng(seed)
-    edge = [0, 1, 7, 8, 63, 64, nq - 9, nq - 8, nq - 2, nq - 1]
-    return sorted(set([i for i in edge if 0 <= i < nq] + list(rng.choice(nq, size=min(n, nq), replace=False))))
-
-
 TOPK_WORKLOADS = [n for n, c in CONFIGS.items() if c.support != "block_union"]
 
 
@@ -69,11 +63,10 @@ def test_workload_parity(name):
     res = run_page(w)
     ref = oracle_items(w)
     compare_items(res, ref)
-    queries = list(range(cfg.nq)) if cfg.nq * cfg.hkv <= 4096 else _sample(cfg.nq)
-    O, L = oracle_attention(w, ref["S"], queries)
-    mx, mean, nrms = check_close(res["out"][queries], O, cfg.kv_dtype, name)
-    check_lse(res["lse"][queries], L, name)
-    print(f"[page-union] {name}: items={res['n_items']} rows={len(queries)} max_abs={mx:.3e} "
+    O, L = oracle_attention(w, ref["S"])                # every row
+    mx, mean, nrms = check_close(res["out"], O, cfg.kv_dtype, name)
+    check_lse(res["lse"], L, name)
+    print(f"[page-union] {name}: items={res['n_items']} rows={cfg.nq * cfg.hq} max_abs={mx:.3e} "
           f"mean_abs={mean:.3e}", flush=True)
 
 
@@ -119,10 +112,9 @@ def test_headline_workload_wide_items():
     res = run_page(w, chunk=16)
     ref = oracle_items(w, chunk=16)
     compare_items(res, ref)
-    queries = _sample(cfg.nq, seed=1)
-    O, L = oracle_attention(w, ref["S"], queries)
-    check_close(res["out"][queries], O, cfg.kv_dtype, "c3 chunk 16")
-    check_lse(res["lse"][queries], L, "c3 chunk 16")
+    O, L = oracle_attention(w, ref["S"])
+    check_close(res["out"], O, cfg.kv_dtype, "c3 chunk 16")
+    check_lse(res["lse"], L, "c3 chunk 16")
 
 
 def test_future_pages_and_empty_supports():
