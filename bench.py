@@ -74,52 +74,251 @@ def calibrate_copy(mib: int) -> None:
     print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
 
 
+def item_members(group_qids, n_tables: int, max_group: int, nq: int) -> np.ndarray:
+    """Member query IDs of every work item, int64 [n_tables, max_group], -1 padded: the
+    listed groups, or consecutive groups of max_group IDs per KV head when group_qids is
+    None (the original-order groups)."""
+    if group_qids is not None:
+        return np.asarray(group_qids, dtype=np.int64).reshape(n_tables, max_group)
+    n_groups_g = -(-nq // max_group)
+    j = np.arange(n_tables) % n_groups_g
+    ids = j[:, None] * max_group + np.arange(max_group)[None, :]
+    return np.where(ids < nq, ids, -1)
+
+
+def union_table_stats(union_off, union_qmask, members) -> dict:
+    """Page visits and member x page slots of query-union tables (PageWeaver Fig. 2 and
+    Fig. 6 counts): visits = sum |U|, slots = sum |g| |U|, selected = member-mask bits set,
+    masked = slots - selected."""
+    sizes = np.diff(np.asarray(union_off, dtype=np.int64))
+    gsz = (np.asarray(members) >= 0).sum(axis=1)
+    qm = np.asarray(union_qmask[:int(sizes.sum())], dtype=np.uint8)
+    selected = int(np.unpackbits(qm[:, None], axis=1).sum())
+    slots = int((sizes * gsz).sum())
+    return {"visits": int(sizes.sum()), "slots": slots, "selected": selected,
+            "masked": slots - selected, "masked_frac": (slots - selected) / slots if slots else 0.0}
+
+
+def row_tile_work(union_off, union_pages, union_qmask, members, q_pos, G: int, ps: int,
+                  kv_len: int, shared_table: bool = False, n_split: int = 1) -> dict:
+    """The attention's unit of MFMA work is a row tile (16 query-head rows: 16 / G members)
+    against a 32-token tile of a union page.  It runs when some member of the row tile
+    selected the page (member-mask bit) and the tile starts at or before the row tile's
+    last usable token; otherwise it is skipped.  Counts both, from the tables alone.
+    members: [n_items, max_group] query IDs (-1 padded); shared_table: every item of KV
+    head g reads table g (then no member masks)."""
+    members = np.asarray(members, dtype=np.int64)
+    n_items, max_group = members.shape
+    off = np.asarray(union_off, dtype=np.int64)
+    rows = max_group * G
+    n_rt = -(-rows // 16)
+    # member bits of each row tile, and its last usable token (-1: no valid row)
+    qp = np.asarray(q_pos, dtype=np.int64)
+    lim_m = np.where(members >= 0, np.minimum(qp[np.maximum(members, 0)], kv_len - 1), -1)
+    rt_bits = np.zeros(n_rt, dtype=np.int64)
+    rt_lim = np.full((n_items, n_rt), -1, dtype=np.int64)
+    for t in range(n_rt):
+        ms = sorted({r // G for r in range(16 * t, min(16 * (t + 1), rows))})
+        for m in ms:
+            rt_bits[t] |= 1 << m
+        rt_lim[:, t] = lim_m[:, ms].max(axis=1)
+    n_tables = len(off) - 1
+    active = total = 0
+    sub = ps // 32
+    for it in range(n_items):
+        e = (it // (n_items // n_tables)) if shared_table else it
+        pages = np.asarray(union_pages[off[e]:off[e + 1]], dtype=np.int64)
+        if pages.size == 0:
+            continue
+        qm = (np.full(pages.size, 0xFF, dtype=np.int64) if union_qmask is None
+              else np.asarray(union_qmask[off[e]:off[e + 1]], dtype=np.int64))
+        tok0 = pages[:, None] * ps + 32 * np.arange(sub)[None, :]                 # [P, sub]
+        for t in range(n_rt):
+            if rt_lim[it, t] < 0:
+                continue
+            sel = (qm & (rt_bits[t] if union_qmask is not None else 0xFF)) != 0
+            act = sel[:, None] & (tok0 <= rt_lim[it, t])
+            active += int(act.sum())
+            total += tok0.size
+    return {"active_pairs": active, "pairs": total, "row_tiles": n_rt}
+
+
 def unique_kv_bytes(union_pages_total: int, cfg) -> int:
     esz = 1 if cfg.kv_dtype == "fp8" else 2
     per_page = 2 * cfg.ps * cfg.d * esz + (8 if cfg.kv_dtype == "fp8" else 0)
     return union_pages_total * per_page
 
 
-def cpu_baseline(w, n_queries: int) -> dict:
-    """The oracle as it stands on the first n_queries queries (whole windows), 1 thread."""
-    from threadpoolctl import threadpool_limits
+def host_cores() -> int:
+    """Cores this process may run on, at most 16 (a one-GPU share of the host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
+
+def blas_vendor() -> str:
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()
+                if i.get("user_api") == "blas"]
+        return ", ".join(libs) or "unknown"
+    except Exception:          # the report only; never fails the run
+        return "unknown"
+
+
+def cpu_baseline(w, n_queries: int, cores: int) -> tuple:
+    """The oracle as it stands on the first n_queries queries (whole windows): pure-Python
+    bitsets, grouping and union tables, then route A (the definition) for every row with
+    its KV heads and query batches spread over `cores` threads.  Returns the record and the
+    route A output (fp64 [n, hq, d]) for the accuracy check."""
     from oracle import attention, prep
     cfg = w.cfg
     nqs = min(cfg.nq, max(cfg.window, (n_queries // cfg.window) * cfg.window))
-    topk = w.topk[:nqs]
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
+    t0 = time.perf_counter()
+    if w.topk is not None:
+        topk = w.topk[:nqs]
         bits = prep.page_bitsets(topk, cfg.n_pages)
         groups = [prep.group_affinity(b, cfg.window, cfg.max_group) for b in bits]
         prep.union_tables(bits, groups)
-        t1 = time.perf_counter()
         S = prep.supports(topk, cfg.n_pages)
-        attention.route_a(w.q[:nqs], w.k, w.v, w.k_scale, w.v_scale, cfg.kv_dtype, S, w.q_pos[:nqs],
-                          cfg.kv_len, cfg.ps, 1.0 / math.sqrt(cfg.d))
-        t2 = time.perf_counter()
-    return {"value": nqs / (t2 - t0), "unit": "queries/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {nqs} of {cfg.nq} queries ({nqs // cfg.window} windows of {cfg.window}), "
-                      f"all {cfg.hkv} KV heads; prep {t1 - t0:.2f}s + attention {t2 - t1:.2f}s",
-            "cpu": _cpu_model()}
+    else:   # block union: the per-KV-group tables, every query over its group's table
+        S = attention.shared_supports(prep.block_tables(w.mask_rows, cfg.n_pages), nqs)
+    t1 = time.perf_counter()
+    O, _ = attention.route_a_batched(w.q[:nqs], w.k, w.v, w.k_scale, w.v_scale, cfg.kv_dtype, S,
+                                     w.q_pos[:nqs], cfg.kv_len, cfg.ps, 1.0 / math.sqrt(cfg.d),
+                                     workers=cores)
+    t2 = time.perf_counter()
+    rec = {"value": nqs / (t2 - t0), "unit": "queries/s", "cores": min(cores, cfg.hkv * -(-nqs // 64)),
+           "kind": "oracle",
+           "sample": f"first {nqs} of {cfg.nq} queries ({nqs // cfg.window} windows of {cfg.window}), "
+                     f"all {cfg.hkv} KV heads; prep {t1 - t0:.2f}s (pure Python, one thread) + "
+                     f"attention {t2 - t1:.2f}s (numpy fp64 route A, {cores} threads)",
+           "cpu": _cpu_model(), "blas": blas_vendor(), "prep_s": t1 - t0, "attention_s": t2 - t1}
+    return rec, O
 
 
-def profiled_traffic(workload: str):
-    """HBM-side bytes per attention launch from the committed rocprofv3 summary
-    (FETCH_SIZE + WRITE_SIZE, scaled by a plain-copy calibration), or None if the
-    kernel source changed since the counters were taken."""
+def accuracy(out_bf16, ref) -> dict:
+    """max-abs, mean-abs and NRMS (PageWeaver Table 2: ||O - R|| / ||R|| over the whole
+    output, in percent) of the GPU output against the oracle's rows."""
+    got = out_bf16.astype(np.float64)
+    err = np.abs(got - ref)
+    den = float(np.sqrt((ref ** 2).sum()))
+    return {"rows": int(ref.shape[0] * ref.shape[1]), "elements": int(ref.size),
+            "max_abs": float(err.max()), "mean_abs": float(err.mean()),
+            "nrms_pct": 100.0 * float(np.sqrt((err ** 2).sum())) / den if den else 0.0,
+            "finite": bool(np.isfinite(got).all())}
+
+
+MFMA_PEAK_FLOPS = {"bf16": 2.5e15, "fp8": 5.0e15}   # dense, per the MI355X specification
+FLOPS_PER_MOP = 512                                   # SQ_INSTS_VALU_MFMA_MOPS_* unit
+
+
+def attn_source_hash() -> str:
     import hashlib
-    import re
     src = os.path.join(ROOT, "query_union_kv_amd", "csrc", "attn.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def profiled_counters(workload: str):
+    """Per-launch counters of the attention kernel from the committed rocprofv3 summary
+    profiles/k_attn_<workload>.md (a line `counters_per_launch = {json}  (attn.hip
+    sha256[:16] H)`), or None when the summary is missing or the kernel source has changed
+    since the counters were taken.  Keys: fetch_bytes and write_bytes (FETCH_SIZE and
+    WRITE_SIZE scaled by a plain-copy calibration), mops_bf16 / mops_f8 (MFMA work, 512
+    flops each), valu_busy (SQ_ACTIVE_INST_VALU x 4 cycles per SIMD over the kernel's
+    cycles), l2_hit (TCC_HIT / (TCC_HIT + TCC_MISS)), mean_us (kernel trace)."""
+    import re
     summ = os.path.join(ROOT, "profiles", f"k_attn_{workload}.md")
     if not os.path.exists(summ):
         return None
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    h = attn_source_hash()
     for line in open(summ):
-        m = re.match(r"traffic_bytes_per_launch\[.*\] = ([0-9.eE+]+)\s+\(attn.hip sha256\[:16\] (\w+)\)", line)
+        m = re.match(r"counters_per_launch = (\{.*\})\s+\(attn.hip sha256\[:16\] (\w+)\)", line.strip())
         if m and m.group(2) == h:
-            return float(m.group(1))
+            return json.loads(m.group(1))
     return None
+
+
+def read_peaks(dev, reps: int = 5) -> dict:
+    """Measured read rates of plain streaming-read kernels (libpw_probe.so) by the level
+    that serves them, in GB/s (best of `reps` launches): `vec` = vector loads, `lds` =
+    direct global->LDS loads (the attention's load path).  Working sets: 2 MiB (every XCD
+    re-reads it from its L2), 128 MiB (re-read from the 256 MB last-level cache once
+    warm: each XCD's share, 16 MiB, exceeds its 4 MB L2), 4 GiB (HBM)."""
+    import ctypes
+
+    import torch
+    L = ctypes.CDLL(os.path.join(ROOT, "query_union_kv_amd", "libpw_probe.so"))
+    L.pwp_read.restype = ctypes.c_int
+    L.pwp_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                           ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    out = {}
+    for name, nbytes, seg, n_blocks in (("l2", 2 << 20, 64 << 10, 16384),
+                                        ("mall", 128 << 20, 64 << 10, 8192),
+                                        ("hbm", 4 << 30, 1 << 20, 4096)):
+        buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        out[name] = {"buffer_bytes": nbytes, "bytes_per_launch": seg * n_blocks}
+        for mode, key in ((0, "vec"), (1, "lds")):
+            best = None
+            for r in range(reps + 1):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                st = L.pwp_read(buf.data_ptr(), nbytes, seg, n_blocks, mode, sink.data_ptr(),
+                                stream.cuda_stream)
+                e1.record(stream)
+                if st != 0:
+                    raise RuntimeError(f"pwp_read failed: {st}")
+                torch.cuda.synchronize()
+                if r:   # the first launch warms the caches
+                    t = e0.elapsed_time(e1)
+                    best = t if best is None else min(best, t)
+            out[name][key + "_GBs"] = seg * n_blocks / (best / 1e3) / 1e9
+        del buf
+    return out
+
+
+def roofline_levels(Bu: float, t_attn_s: float, ctr, peaks) -> dict:
+    """The attention kernel against each resource that could bound it.
+      logical: the union bytes B_u (every group's union read once) over the kernel time,
+               against the 8 TB/s HBM peak - not a bound: the re-reads of pages that other
+               groups also read come from the caches, so this may exceed 1;
+      hbm:     counter-measured bytes between the L2 and memory (FETCH_SIZE + WRITE_SIZE,
+               calibrated) against 8 TB/s;
+      mfma:    counter-measured MFMA work (MOPS) as the time the matrix cores need at their
+               dense peak (bf16 2.5, fp8 5.0 PFLOP/s) over the kernel time;
+      valu:    counter-measured vector-ALU issue cycles over the kernel's SIMD cycles;
+      cache:   B_u over the kernel time against the measured read rate of a plain
+               streaming read of the level that serves it (the L2 hit fraction h from the
+               counters: 1 / (h / L2 rate + (1 - h) / last-level rate), with the
+               direct-to-LDS load path's rates)."""
+    lv = {"logical": {"achieved": Bu / t_attn_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": Bu / t_attn_s / 1e9 / HBM_PEAK_GBS, "bound": False,
+                      "what": "union bytes B_u / kernel time vs HBM peak (not a bound: cache-served re-reads)"}}
+    if ctr:
+        hb = ctr["fetch_bytes"] + ctr["write_bytes"]
+        lv["hbm"] = {"achieved": hb / t_attn_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": hb / t_attn_s / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": hb,
+                     "what": "FETCH_SIZE + WRITE_SIZE (calibrated) per launch / kernel time"}
+        fb, f8 = ctr["mops_bf16"] * FLOPS_PER_MOP, ctr["mops_f8"] * FLOPS_PER_MOP
+        t_peak = fb / MFMA_PEAK_FLOPS["bf16"] + f8 / MFMA_PEAK_FLOPS["fp8"]
+        lv["mfma"] = {"achieved": (fb + f8) / t_attn_s / 1e12,
+                      "peak": (fb + f8) / t_peak / 1e12 if t_peak else MFMA_PEAK_FLOPS["bf16"] / 1e12,
+                      "unit": "TFLOP/s", "frac": t_peak / t_attn_s, "flops_per_launch": fb + f8,
+                      "flops_bf16": fb, "flops_fp8": f8,
+                      "what": "MFMA MOPS x 512 per launch; peak = dtype-weighted dense peak"}
+        if ctr.get("valu_busy") is not None:
+            lv["valu"] = {"achieved": ctr["valu_busy"], "peak": 1.0, "unit": "fraction of SIMD cycles",
+                          "frac": ctr["valu_busy"], "what": "vector-ALU issue cycles / SIMD cycles (counters)"}
+        h = ctr.get("l2_hit")
+        if peaks and h is not None:
+            p_l2, p_llc = peaks["l2"]["lds_GBs"], peaks["mall"]["lds_GBs"]
+            p_eff = 1.0 / (h / p_l2 + (1.0 - h) / p_llc)
+            lv["cache"] = {"achieved": Bu / t_attn_s / 1e9, "peak": p_eff, "unit": "GB/s",
+                           "frac": Bu / t_attn_s / 1e9 / p_eff, "l2_hit": h,
+                           "l2_read_GBs": p_l2, "llc_read_GBs": p_llc,
+                           "what": "B_u / kernel time vs measured L2 / last-level read rates, "
+                                   "weighted by the counter-measured L2 hit fraction"}
+    return lv
 
 
 def _cpu_model() -> str:
@@ -213,6 +412,7 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    out_final = out.float().cpu().numpy()       # the timed calls' output (every call writes the same)
     t_prep = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)]
     t_attn = [evs[i][1].elapsed_time(evs[i][2]) for i in range(args.steps)]
     ms_step = wall * 1e3 / args.steps
@@ -242,12 +442,16 @@ def main():
               "t_attn_ms_median": statistics.median(t_attn), "union_pages": total_pages,
               "page_visits": visits,
               "unique_kv_bytes": Bu}
+    n_items = len(off) - 1 if mode == "topk" else cfg.hkv * plan.n_groups
+    members = item_members(plan.group_qids.cpu().numpy() if plan.group_qids is not None else None,
+                           n_items, max_group, cfg.nq)
+    pages_np = plan.union_pages[:total_pages].cpu().numpy()
+    qm_np = plan.union_qmask[:total_pages].cpu().numpy() if plan.union_qmask is not None else None
+    work = row_tile_work(off, pages_np, qm_np, members, w.q_pos, cfg.g, cfg.ps, cfg.kv_len,
+                         shared_table=(mode != "topk"))
     if mode == "topk":
-        sizes = np.diff(off)
-        gsz = plan.group_size.cpu().numpy().reshape(-1)
-        qm = plan.union_qmask[:total_pages].cpu().numpy()
-        selected = int(np.unpackbits(qm[:, None], axis=1).sum())      # retained selected edges
-        slots = int((sizes * gsz).sum())                                # member x union-page slots
+        st = union_table_stats(off, qm_np, members)
+        selected, slots = st["selected"], st["slots"]                  # retained edges, member x page slots
         orig = pw.SparsePrefill(nq=cfg.nq, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, n_pages=cfg.n_pages,
                                 page_size=cfg.ps, kv_len=cfg.kv_len, k=ids.shape[2], window=cfg.window,
                                 max_group=cfg.max_group, grouping="original", device=dev)
@@ -289,7 +493,6 @@ def main():
                              "fixed_affinity_attention": t_fixed, "online_affinity_call": t_online,
                              "execution_saving": t_orig_attn - t_fixed,
                              "online_cost": t_online - t_fixed, "net_saving": t_orig - t_online}
-        exec_rows_pages = float((sizes * gsz).sum()) * cfg.g     # (row, union page) pairs
 
         # Grouping window sweep: a wider bounded search finds more same-community queries
         # (fewer page visits) but costs more preparation.
@@ -366,11 +569,62 @@ def main():
             "max_abs_vs_union": float((out_pu.float() - out.float()).abs().max().item())}
         del pu, out_pu
     else:
-        exec_rows_pages = float(visits) * max_group * cfg.g      # item rows x its table pages
-    # executed MFMA work: QK and PV, 2 flops per MAC, over every (row, union token)
-    exec_flops = 4.0 * cfg.d * cfg.ps * exec_rows_pages
-    extras["executed_tflops"] = exec_flops / (attn_ms / 1e3) / 1e12
+        # CompactAttention's shared per-KV-group tables: the timed form cuts each table into
+        # plan.n_split slices (partial rows merged by lse); the same attention with no
+        # partials at all (one workgroup streams a whole table) is timed beside it
+        one = pw.SparsePrefill(nq=cfg.nq, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, n_pages=cfg.n_pages,
+                               page_size=cfg.ps, kv_len=cfg.kv_len, k=ids.shape[2], max_group=max_group,
+                               mode=mode, n_rows=ids.shape[0], n_split=1, device=dev)
+        one.prepare(ids, stream)
+        out_one = torch.empty_like(q)
+        for _ in range(20):
+            one.attend(q, kc, vc, q_pos, out_one, ks, vs, stream=stream)
+        t_one = timed(lambda: one.attend(q, kc, vc, q_pos, out_one, ks, vs, stream=stream), n=20)
+        extras["shared_table"] = {
+            "timed_form": f"table cut into {plan.n_split} slices, partial rows merged by lse"
+                          if plan.n_split > 1 else "one workgroup per table slice: no partials",
+            "n_split": plan.n_split, "attn_ms": attn_ms,
+            "no_partials": {"n_split": 1, "attn_ms": t_one, "call_ms": statistics.mean(t_prep) + t_one,
+                            "queries_per_s": cfg.nq / ((statistics.mean(t_prep) + t_one) / 1e3),
+                            "max_abs_vs_timed": float((out_one.float() - out.float()).abs().max().item())}}
+        del one, out_one
+    # executed MFMA work: QK and PV over every row tile x 32-token tile the kernel runs (the
+    # tables' member masks and causal limits decide which); skipped pairs are not counted.
+    # (fp8 K at d = 128 runs QK as two fp8 MFMAs, hi and lo parts of Q: the counters count both)
+    exec_flops = 2 * 2.0 * 16 * 32 * cfg.d * work["active_pairs"]
+    extras["executed_mfma"] = {"row_tile_key_tile_pairs": work["active_pairs"],
+                               "pairs_in_tables": work["pairs"],
+                               "skipped": work["pairs"] - work["active_pairs"],
+                               "flops_per_launch": exec_flops,
+                               "tflops": exec_flops / (attn_ms / 1e3) / 1e12}
+    if mode == "topk":
+        extras["executed_mfma"]["executed_over_useful"] = exec_flops / useful_flops
     extras["attn_queries_per_s"] = cfg.nq / (attn_ms / 1e3)
+
+    # ---- the complete call captured once in a HIP graph and replayed, against eager calls
+    # (PageWeaver times graph replays beside eager rounds: Table 1, Fig. 8) -----------------
+    out_g = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan.prepare(ids)
+        plan.attend(q, kc, vc, q_pos, out_g, ks, vs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.prepare(ids)
+        plan.attend(q, kc, vc, q_pos, out_g, ks, vs)
+    for _ in range(20):
+        graph.replay()
+    t_graph = timed(graph.replay, n=50)
+    t_eager = timed(step, n=50)
+    torch.cuda.synchronize()
+    extras["hip_graph"] = {"graph_call_ms": t_graph, "eager_call_ms": t_eager,
+                           "queries_per_s_graph": cfg.nq / (t_graph / 1e3),
+                           "bit_identical": bool(torch.equal(out_g.view(torch.int16), out.view(torch.int16))),
+                           "what": "bitsets, grouping, union tables and attention as one graph, 50 replays"}
+    del graph, out_g
 
     # ---- the step before attention: appending the chunk's own keys and values -------------
     # (into copies of the caches, so the attention inputs above stay as generated)
@@ -470,6 +724,23 @@ def main():
     extras["copy_peak"] = {"GBs": copy_gbs, "unique_kv_frac_of_copy": achieved / copy_gbs,
                            "what": "1 GiB device-to-device copy, read + write bytes, best of 5"}
 
+    # ---- measured read rates of each memory level, and the roofline levels -------------------
+    peaks = read_peaks(dev)
+    extras["read_peaks_GBs"] = peaks
+    ctr = profiled_counters(cfg.name)
+    levels = roofline_levels(Bu, attn_ms / 1e3, ctr, peaks)
+    bounds = {k: v for k, v in levels.items() if k != "logical"}
+    bound = max(bounds, key=lambda k: bounds[k]["frac"]) if bounds else "logical"
+    top = levels[bound]
+    if ctr:
+        levels["counters"] = {"source": f"profiles/k_attn_{cfg.name}.md", "attn_sha16": attn_source_hash(),
+                              "profiled_mean_us": ctr.get("mean_us"),
+                              "frac_at_profiled_time": {k: v["frac"] * attn_ms * 1e3 / ctr["mean_us"]
+                                                        for k, v in bounds.items() if ctr.get("mean_us")}}
+    else:
+        levels["counters"] = {"source": None, "note": "no counters for this kernel source: only the "
+                                                      "logical and measured-cache levels are known"}
+
     # arithmetic of the attention's MFMAs: fp8 KV with d = 128 takes QK on the fp8 MFMA
     dtype = "fp8/bf16" if cfg.kv_dtype == "fp8" and cfg.d == 128 else "bf16"
     rec = {
@@ -478,14 +749,28 @@ def main():
         "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "hq": cfg.hq, "hkv": cfg.hkv, "d": cfg.d, "page_size": cfg.ps,
                    "kv_len": cfg.kv_len, "nq": cfg.nq, "topk": cfg.k, "kv_dtype": cfg.kv_dtype,
-                   "window": cfg.window, "max_group": max_group, "seed": w.seed},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(cfg.name), "kernel": "k_attn",
-                     "bytes_per_launch": Bu},
+                   "window": cfg.window, "max_group": max_group, "seed": w.seed,
+                   "attention": ("query unions with member masks (pw_sparse_prefill)" if mode == "topk" else
+                                 f"shared per-KV-group tables, {plan.n_split} slices per table merged by lse"
+                                 if plan.n_split > 1 else "shared per-KV-group tables, no partials")},
+        "roofline": {"bound": bound, "achieved": top["achieved"], "peak": top["peak"], "unit": top["unit"],
+                     "frac": top["frac"],
+                     "traffic": (ctr["fetch_bytes"] + ctr["write_bytes"]) if ctr else None,
+                     "kernel": "k_attn", "kernel_ms": attn_ms, "union_bytes_per_launch": Bu,
+                     "levels": levels},
         "extra": extras,
     }
-    if not args.no_cpu and mode == "topk":
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_queries)
+    if not args.no_cpu:
+        cpu, ref = cpu_baseline(w, args.cpu_queries, host_cores())
+        rec["cpu_baseline"] = cpu
+        n = ref.shape[0]
+        acc = accuracy(out_final[:n], ref)
+        tol = (2e-2, 2e-3) if cfg.kv_dtype == "bf16" else (6e-2, None)
+        acc["within_tolerance"] = bool(acc["finite"] and acc["max_abs"] <= tol[0]
+                                       and (tol[1] is None or acc["mean_abs"] <= tol[1]))
+        acc["tolerance"] = {"max_abs": tol[0], "mean_abs": tol[1]}
+        acc["oracle"] = "route A (per-query gather, fp64), every row of the sample"
+        extras["accuracy"] = acc
     print(json.dumps(rec), flush=True)
 
 

@@ -10,6 +10,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libpw.so")
+# read-bandwidth probes used by the benchmark (not part of the library's method)
+PROBE_LIB = os.path.join(HERE, "libpw_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "kvcache.hip", "prep.hip", "pageunion.hip", "attn.hip"]
@@ -57,6 +60,14 @@ def build(verbose: bool = False, jobs: int = 3) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    pobjs = []
+    for src in PROBE_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        _run([hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        pobjs.append(obj)
+    tmp = PROBE_LIB + ".tmp"
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *pobjs, "-o", tmp], verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 
