@@ -296,6 +296,28 @@ pw_status pw_shared_table_prefill(const void* q, int nq, int hq, int hkv, int d,
                                   int64_t capacity, int n_split, void* partial_o,
                                   float* partial_lse, void* out, float* lse, hipStream_t stream);
 
+/* ---- (4c) pw_shared_table_prefill allocating nothing -----------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Exactly pw_shared_table_prefill (the
+ * same kernels, the same result bit for bit), but the slice partials live in a device array
+ * that the library owns: pw_noalloc_scratch_bytes() = 32 MiB on each device the call runs
+ * on (the current device, which must be the stream's), held until the process ends and
+ * looked up once per device.  Arguments as pw_shared_table_prefill without partial_o and
+ * partial_lse.  PW_ERR_CAPACITY, with nothing enqueued, when the partials - nq*hq*n_split
+ * bf16 rows of d (rounded up to 256 bytes) plus nq*hq*n_split fp32 - exceed the array;
+ * n_split = 1 uses none of it.  Every call on a device shares its array: calls that
+ * overlap in time on one GPU race.  Nothing in it needs clearing (each call writes every
+ * partial row before merging it).                                                        */
+size_t pw_noalloc_scratch_bytes(void);
+pw_status pw_shared_table_prefill_noalloc(const void* q, int nq, int hq, int hkv, int d,
+                                          const void* k_cache, const void* v_cache, int kv_dtype,
+                                          const float* k_scale, const float* v_scale, int page_size,
+                                          int n_pages, int64_t stride_head, int64_t stride_page,
+                                          const int32_t* q_pos, int kv_len, float sm_scale,
+                                          int max_group, const int32_t* union_off,
+                                          const int32_t* union_pages, int64_t capacity, int n_split,
+                                          void* out, float* lse, hipStream_t stream);
+
 /* ---- (5) direct KV-page union (page-major execution) -----------------------------------
  * PageWeaver abstract: the page-major alternative to query unions visits every
  * (KV head, page) once for all queries that selected it, and pays for it with

@@ -69,6 +69,9 @@ def lib() -> ctypes.CDLL:
             "pw_schedule_items": (I, [P, I, P, P]),
             "pw_shared_table_prefill": (I, [P, I, I, I, I, P, P, I, P, P, I, I, I64, I64, P, I, F,
                                             I, P, P, I64, I, P, P, P, P, P]),
+            "pw_shared_table_prefill_noalloc": (I, [P, I, I, I, I, P, P, I, P, P, I, I, I64, I64, P, I,
+                                                    F, I, P, P, I64, I, P, P, P]),
+            "pw_noalloc_scratch_bytes": (ctypes.c_size_t, []),
             "pw_page_items_capacity": (I64, [I, I, I, I, I]),
             "pw_page_workspace_bytes": (ctypes.c_size_t, [I, I, I]),
             "pw_page_tables": (I, [P, I, I, I, I, I, P, ctypes.c_size_t, P, P, P, P, P, P, I64, P]),
@@ -337,6 +340,30 @@ def pw_shared_table_prefill(q, k_cache, v_cache, q_pos, kv_len: int, union_off, 
         union_pages.numel(), n_split, _ptr(partial_o, torch.bfloat16, "partial_o"),
         _ptr(partial_lse, torch.float32, "partial_lse"), _ptr(out, torch.bfloat16, "out"),
         _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
+def pw_shared_table_prefill_noalloc(q, k_cache, v_cache, q_pos, kv_len: int, union_off, union_pages,
+                                    out, *, hkv: int, max_group: int, n_split: int, k_scale=None,
+                                    v_scale=None, sm_scale: Optional[float] = None, lse=None,
+                                    stream=None) -> None:
+    """pw_shared_table_prefill with the slice partials in the library's own device array
+    (pw_noalloc_scratch_bytes() per device): no device memory is allocated for the call.
+    Calls that overlap in time on one GPU share that array and race."""
+    nq, hq, d = q.shape
+    _, n_pages, page_size, _ = k_cache.shape
+    sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    _check(lib().pw_shared_table_prefill_noalloc(
+        _ptr(q, torch.bfloat16, "q"), nq, hq, hkv, d, _ptr(k_cache, name="k_cache"),
+        _ptr(v_cache, name="v_cache"), _cache_dtype(k_cache), _ptr(k_scale, torch.float32, "k_scale"),
+        _ptr(v_scale, torch.float32, "v_scale"), page_size, n_pages, n_pages * page_size * d,
+        page_size * d, _ptr(q_pos, torch.int32, "q_pos"), kv_len, sm, max_group,
+        _ptr(union_off, torch.int32, "union_off"), _ptr(union_pages, torch.int32, "union_pages"),
+        union_pages.numel(), n_split, _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"),
+        _stream(stream)))
+
+
+def pw_noalloc_scratch_bytes() -> int:
+    return lib().pw_noalloc_scratch_bytes()
 
 
 def pw_page_items_capacity(nq: int, hkv: int, k_max: int, n_pages: int, chunk: int) -> int:

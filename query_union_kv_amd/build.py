@@ -15,7 +15,7 @@ PROBE_LIB = os.path.join(HERE, "libpw_probe.so")
 PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "kvcache.hip", "prep.hip", "pageunion.hip", "attn.hip"]
+SOURCES = ["api.cpp", "kvcache.hip", "prep.hip", "pageunion.hip", "attn.hip", "noalloc.hip"]
 # Packed fp32 ops are disabled for every device compile on this hardware.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
