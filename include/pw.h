@@ -55,6 +55,14 @@ const char* pw_version(void);
 /* Text of the last non-OK status returned on this thread ("" if none). */
 const char* pw_last_error(void);
 
+/* Debug builds (libpw_debug.so, compiled with -DPW_DEBUG): the kernels count every lane at
+ * which an index or LDS-ring invariant does not hold (table offsets inside capacity and
+ * ascending, listed pages valid, a tile's loads inside its ring stage, listed members
+ * queries of the chunk, output rows in range, union entries within capacity, page-major
+ * items within their bound), without trapping; this returns the count since the last call
+ * and clears it (synchronous; -1 on a HIP error).  Release builds return -2.            */
+int64_t pw_debug_violations(void);
+
 /* 64-bit words per page bitset row: ceil(n_pages / 64). */
 int pw_words(int n_pages);
 

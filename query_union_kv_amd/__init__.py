@@ -29,6 +29,8 @@ __all__ = [
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpw.so")
+# the same library built with -DPW_DEBUG: device-side invariant counters (pw_debug_violations)
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpw_debug.so")
 PW_KV_BF16 = 0
 PW_KV_FP8_E4M3 = 1
 _STATUS = {0: "PW_OK", -1: "PW_ERR_ARG", -2: "PW_ERR_UNSUPPORTED", -3: "PW_ERR_CAPACITY",
@@ -54,6 +56,7 @@ def lib() -> ctypes.CDLL:
         P, I, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
         sig = {
             "pw_version": (ctypes.c_char_p, []),
+            "pw_debug_violations": (I64, []),
             "pw_last_error": (ctypes.c_char_p, []),
             "pw_words": (I, [I]),
             "pw_num_groups": (I, [I, I, I]),
@@ -111,6 +114,20 @@ def _stream(stream) -> int:
 
 def pw_version() -> str:
     return lib().pw_version().decode()
+
+
+def pw_debug_violations() -> int:
+    """Invariant violations counted by a debug build since the last call (then cleared);
+    -2 from a release build."""
+    return lib().pw_debug_violations()
+
+
+def use_library(path: str) -> None:
+    """Makes the binding call the library at `path` from now on (e.g. DEBUG_LIB_PATH)."""
+    global _lib, LIB_PATH
+    LIB_PATH = path
+    _lib = None
+    lib()
 
 
 def pw_words(n_pages: int) -> int:
@@ -494,7 +511,8 @@ class SparsePrefill:
     two halves, each over the union of its own members' pages (a page both halves
     selected is read twice): every row sees the same pages in the same order, so
     the outputs are bit-identical, and wide groups (8 members x 8 query heads)
-    avoid the two-wave form, whose waves wait on each other's tiles.
+    avoid the two-wave form, whose waves wait on each other's tiles.  The default
+    (``halves=None``) runs groups of more than 32 query-head rows as halves.
     Block-union mode (``mask_rows`` given, CompactAttention's per-KV-group
     block table): bitsets of the mask rows -> one union over every row of a
     KV head -> attention of consecutive query groups over that shared table;
@@ -520,14 +538,18 @@ class SparsePrefill:
                                 # give every SIMD two waves; 1: no partials)
     schedule: bool = True       # topk mode: start the largest unions first (the work order of
                                 # pw_schedule_items; listed by pw_prepare when fused)
-    halves: bool = False        # topk mode: run each group as two halves of max_group / 2
+    halves: Optional[bool] = None   # topk mode: run each group as two halves of max_group / 2
                                 # members, each over the union of its own members' pages
+                                # (None: when a group has more than 32 query-head rows)
     device: str = "cuda"
 
     def __post_init__(self):
         dev = self.device
         w = pw_words(self.n_pages)
         i32 = dict(dtype=torch.int32, device=dev)
+        if self.halves is None:
+            self.halves = (self.mode == "topk" and self.grouping == "affinity" and not self.arrange
+                           and self.max_group % 2 == 0 and self.max_group * (self.hq // self.hkv) > 32)
         if self.halves and (self.mode != "topk" or self.max_group % 2):
             raise ValueError("halves needs topk mode and an even max_group")
         if self.halves and self.arrange:
@@ -722,13 +744,14 @@ class ChunkedPrefill:
 def sparse_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, topk: torch.Tensor,
                    q_pos: torch.Tensor, *, kv_len: int, k_scale: Optional[torch.Tensor] = None,
                    v_scale: Optional[torch.Tensor] = None, window: int = 64, max_group: int = 8,
-                   sm_scale: Optional[float] = None, with_lse: bool = False, halves: bool = False,
+                   sm_scale: Optional[float] = None, with_lse: bool = False,
+                   halves: Optional[bool] = None,
                    stream=None):
     """One complete query-union call on the current stream: bitsets, affinity grouping and
     union tables from topk [nq, hkv, K], then attention.  q bf16 [nq, hq, d]; caches
     [hkv, n_pages, page_size, d] (bf16, or uint8 e4m3fn codes with fp32 scales
     [hkv, n_pages]).  ``halves`` runs every group as two halves over their own unions
-    (the same outputs; see SparsePrefill).  Returns (out, aux): out bf16 [nq, hq, d]; aux
+    (the same outputs; see SparsePrefill; None: for groups of more than 32 rows).  Returns (out, aux): out bf16 [nq, hq, d]; aux
     holds the plan with its bitsets, groups and union tables, and lse [nq, hq] when
     with_lse."""
     nq, hq, d = q.shape

@@ -10,6 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libpw.so")
+# the same library with -DPW_DEBUG (device-side invariant counters)
+DEBUG_LIB = os.path.join(HERE, "libpw_debug.so")
 # read-bandwidth probes used by the benchmark (not part of the library's method)
 PROBE_LIB = os.path.join(HERE, "libpw_probe.so")
 PROBE_SOURCES = ["probe.hip"]
@@ -39,17 +41,20 @@ def _run(cmd, verbose):
         print(out)
 
 
-def build(verbose: bool = False, jobs: int = 3) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    hipcc = _hipcc()
+def _compile_all(hipcc, out_dir, extra, verbose):
+    os.makedirs(out_dir, exist_ok=True)
     objs, procs = [], []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(out_dir, src + ".o")
         objs.append(obj)
-        cmd = [hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    return objs, procs
+
+
+def _finish(hipcc, objs, procs, lib, verbose):
     for cmd, pr in procs:
         out, _ = pr.communicate()
         out = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
@@ -57,9 +62,20 @@ def build(verbose: bool = False, jobs: int = 3) -> str:
             raise RuntimeError(f"build failed: {' '.join(cmd)}\n{out}")
         if verbose and out.strip():
             print(out)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, debug: bool = True) -> str:
+    """libpw.so, libpw_probe.so and (debug=True) libpw_debug.so, the same sources with
+    -DPW_DEBUG: device-side invariant counters, read by pw_debug_violations()."""
+    hipcc = _hipcc()
+    rel = _compile_all(hipcc, BUILD, [], verbose)
+    dbg = _compile_all(hipcc, os.path.join(BUILD, "debug"), ["-DPW_DEBUG"], verbose) if debug else None
+    _finish(hipcc, *rel, LIB, verbose)
+    if dbg:
+        _finish(hipcc, *dbg, DEBUG_LIB, verbose)
     pobjs = []
     for src in PROBE_SOURCES:
         obj = os.path.join(BUILD, src + ".o")

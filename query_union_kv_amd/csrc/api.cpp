@@ -38,6 +38,17 @@ extern "C" {
 
 const char* pw_version(void) { return PW_VERSION; }
 
+int64_t pw_debug_violations(void) {
+#ifdef PW_DEBUG
+  const unsigned long long a = pw::debug_count_attn(), b = pw::debug_count_prep(),
+                           c = pw::debug_count_pageunion();
+  if (a == ~0ull || b == ~0ull || c == ~0ull) return -1;
+  return (int64_t)(a + b + c);
+#else
+  return -2;
+#endif
+}
+
 const char* pw_last_error(void) { return pw::g_err; }
 
 int pw_words(int n_pages) { return n_pages < 0 ? -1 : (n_pages + 63) / 64; }

@@ -44,6 +44,9 @@
 #include "common.h"
 
 namespace pw {
+
+PW_DEBUG_COUNTER_DEFINE(debug_count_attn)
+
 namespace {
 
 constexpr int kWave = 64;
@@ -262,6 +265,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     hq_row = g * p.G + (row - member * p.G);
     id = -1;
     if (member < gsize) id = qids ? qids[member] : j * p.max_group + member;
+    PW_DCHECK(member >= gsize || id < p.nq);   // a listed member is a query of the chunk
     if (id >= p.nq) id = -1;
     slot = -1;
     if (p.out_slot && id >= 0) {
@@ -368,6 +372,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     e_begin = p.union_off[table];
     e_end = p.union_off[table + 1];
   }
+  PW_DCHECK(lane != 0 || (e_begin >= 0 && e_begin <= e_end && e_end <= p.capacity));
   e_begin = min<int64_t>(max<int64_t>(e_begin, 0), p.capacity);
   e_end = min<int64_t>(e_end, p.capacity);
   if (p.n_split > 1) {   // this item's slice of the table
@@ -506,6 +511,9 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       pg_off = (int64_t)max(page_of(t), 0) * p.stride_page_b;
     }
     const int64_t off = pg_off + (int64_t)(t & ((1 << tpp_shift) - 1)) * C::kTensorBytes;
+    // the tile's loads land inside its stage of the ring
+    PW_DCHECK(lane != 0 || (t >= 0 && t < n_tiles && SS >= 0 && SS < ST &&
+                            ((C::kDmaPerTensor - 1) * NW + wave + 1) * kWave * 16 <= C::kTensorBytes));
     const uint8_t* kt = kbase + off;
     const uint8_t* vt = vbase + off;
     constexpr int GN = C::kDmaGroup;
@@ -566,6 +574,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     const int pq = lane_i(md_pq, l);
     PageCtx c;
     c.pg = (pq & 0xFFFFFF) - 1;
+    PW_DCHECK(lane != 0 || (c.pg >= 0 && l >= 0 && l < kWave));   // a listed page, held by the lanes
     c.qm = (int)((uint32_t)pq >> 24);
     c.abits = 0;
 #pragma unroll
@@ -884,6 +893,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       orow = (int64_t)slot * p.G + (hh - g * p.G);
     else if (p.n_split > 1)  // table-slice partial: slot (q, g, slice)
       orow = (((int64_t)id * p.hkv + g) * p.n_split + slice) * p.G + (hh - g * p.G);
+    PW_DCHECK(orow >= 0 && (p.out_slot != nullptr || orow < (int64_t)p.nq * p.hq * max(p.n_split, 1)));
     uint16_t* dst = p.out + orow * D;
 #pragma unroll
     for (int dt = 0; dt < C::kDt; ++dt) {

@@ -6,7 +6,41 @@
 
 #include "../../include/pw.h"
 
+// ---- debug build (-DPW_DEBUG) ------------------------------------------------------------
+// PW_DCHECK(cond) counts, in a device counter of its translation unit, every lane at which
+// an index or ring invariant does not hold (no trap: the kernels still clamp and skip as in
+// the release build, so a violation never faults).  pw_debug_violations() (api.cpp) reads
+// and clears the counters of every translation unit.  Release builds compile it away.
+#ifdef PW_DEBUG
+#define PW_DEBUG_COUNTER_DEFINE(name)                                                   \
+  static __device__ unsigned int pw_dbg_count;                                        \
+  unsigned long long name() {                                                          \
+    unsigned int v = 0, z = 0;                                                         \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(pw_dbg_count), sizeof(v)) != hipSuccess)    \
+      return ~0ull;                                                                    \
+    if (hipMemcpyToSymbol(HIP_SYMBOL(pw_dbg_count), &z, sizeof(z)) != hipSuccess)      \
+      return ~0ull;                                                                    \
+    return v;                                                                          \
+  }
+#define PW_DCHECK(cond)                                      \
+  do {                                                       \
+    if (!(cond)) atomicAdd(&pw_dbg_count, 1u);                \
+  } while (0)
+#else
+#define PW_DEBUG_COUNTER_DEFINE(name)
+#define PW_DCHECK(cond) \
+  do {                  \
+  } while (0)
+#endif
+
 namespace pw {
+
+#ifdef PW_DEBUG
+// per-translation-unit readers of the debug counters (read and clear; ~0 on a HIP error)
+unsigned long long debug_count_attn();
+unsigned long long debug_count_prep();
+unsigned long long debug_count_pageunion();
+#endif
 
 // Records a formatted error message for pw_last_error() and returns `status`.
 pw_status fail(pw_status status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));

@@ -23,6 +23,9 @@
 #include "common.h"
 
 namespace pw {
+
+PW_DEBUG_COUNTER_DEFINE(debug_count_pageunion)
+
 namespace {
 
 constexpr int kWave = 64;
@@ -123,6 +126,7 @@ __global__ __launch_bounds__(256) void k_page_members(
   const int n_gp = hkv * n_pages;
   const int it = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   const int n_items = item_off[n_gp];
+  PW_DCHECK(it != 0 || n_items <= item_capacity);   // the host's item bound held
   if (it >= n_items || it >= item_capacity) return;
   int lo = 0, hi = n_gp;            // last gp with item_off[gp] <= it
   while (hi - lo > 1) {

@@ -16,6 +16,9 @@
 #include "common.h"
 
 namespace pw {
+
+PW_DEBUG_COUNTER_DEFINE(debug_count_prep)
+
 namespace {
 
 constexpr int kWave = 64;
@@ -697,6 +700,7 @@ __device__ void emit_table(const uint64_t* __restrict__ bits, int n_rows, int wo
   }
   const int sh = 16 * (lane & 3);
   int64_t pos = union_off[e];
+  PW_DCHECK(lane != 0 || (pos >= 0 && pos <= union_off[e + 1]));   // prefix sums ascend
   for (int w0 = 0; w0 < words; w0 += kWave / 4) {
     const int w = w0 + (lane >> 2);
     uint32_t mw[8];
@@ -721,6 +725,7 @@ __device__ void emit_table(const uint64_t* __restrict__ bits, int n_rows, int wo
     while (u) {
       const int b = __ffs(u) - 1;
       u &= u - 1;
+      PW_DCHECK(p < capacity);   // (the host's capacity bound held for this table)
       if (p < capacity) {
         union_pages[p] = base + b;
         if (QMASK) {

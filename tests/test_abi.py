@@ -285,3 +285,14 @@ def test_sparse_prefill_rejects_bad_half_groups():
         pw.SparsePrefill(max_group=8, halves=True, arrange=True, **kw)
     with pytest.raises(ValueError):
         pw.SparsePrefill(max_group=8, halves=True, mode="block_union", n_rows=8, **kw)
+
+
+def test_debug_build_loads_and_exports_every_symbol():
+    """libpw_debug.so (-DPW_DEBUG) is built beside libpw.so and exports the same entry
+    points; the release build reports no debug counters (-2, no device call)."""
+    assert os.path.exists(pw.DEBUG_LIB_PATH)
+    D = ctypes.CDLL(pw.DEBUG_LIB_PATH)
+    for n in _declared():
+        assert hasattr(D, n), n
+    L.pw_debug_violations.restype = ctypes.c_int64
+    assert L.pw_debug_violations() == -2
