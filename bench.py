@@ -443,8 +443,10 @@ def main():
               "page_visits": visits,
               "unique_kv_bytes": Bu}
     n_items = len(off) - 1 if mode == "topk" else cfg.hkv * plan.n_groups
-    members = item_members(plan.group_qids.cpu().numpy() if plan.group_qids is not None else None,
-                           n_items, max_group, cfg.nq)
+    halves = mode == "topk" and plan.halves
+    members = item_members((plan.half_qids if halves else plan.group_qids).cpu().numpy()
+                           if plan.group_qids is not None else None,
+                           n_items, plan.width if halves else max_group, cfg.nq)
     pages_np = plan.union_pages[:total_pages].cpu().numpy()
     qm_np = plan.union_qmask[:total_pages].cpu().numpy() if plan.union_qmask is not None else None
     work = row_tile_work(off, pages_np, qm_np, members, w.q_pos, cfg.g, cfg.ps, cfg.kv_len,
@@ -459,6 +461,21 @@ def main():
         torch.cuda.synchronize()
         orig_pages = int(orig.union_off[-1].item())
         per_q = cfg.nq * cfg.hkv
+        group_pages = total_pages          # pages of the affinity groups' unions
+        if halves:                         # (the timed tables are the halves' unions)
+            whole = pw.SparsePrefill(nq=cfg.nq, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, n_pages=cfg.n_pages,
+                                     page_size=cfg.ps, kv_len=cfg.kv_len, k=ids.shape[2], window=cfg.window,
+                                     max_group=cfg.max_group, halves=False, device=dev)
+            whole.prepare(ids)
+            torch.cuda.synchronize()
+            group_pages = int(whole.union_off[-1].item())
+            w_off = whole.union_off.cpu().numpy()
+            st_group = union_table_stats(
+                w_off, whole.union_qmask[:group_pages].cpu().numpy(),
+                item_members(whole.group_qids.cpu().numpy(), len(w_off) - 1, cfg.max_group, cfg.nq))
+            del whole
+        else:
+            st_group = st
         # useful work: keys each (query, head) row actually uses, |J| = sum over its support
         # pages of the tokens at or before its position and before the cache end
         tk = np.asarray(ids_np, dtype=np.int64)                            # [nq, hkv, K]
@@ -474,11 +491,15 @@ def main():
         page_bytes = cfg.ps * cfg.d * (1 if cfg.kv_dtype == "fp8" else 2) * 2 + (8 if cfg.kv_dtype == "fp8" else 0)
         extras.update({
             "useful_tflops": useful_flops / (attn_ms / 1e3) / 1e12,
-            "bytes": {"B_u": Bu, "B_query": selected * page_bytes, "B_orig": orig_pages * page_bytes,
+            "bytes": {"B_u": unique_kv_bytes(group_pages, cfg), "B_streamed": Bu,
+                      "B_query": selected * page_bytes, "B_orig": orig_pages * page_bytes,
                       "B_distinct": int(len(np.unique(np.nonzero(keep)[1] * cfg.n_pages + uniq[keep]))) * page_bytes},
             "visits_per_query_kvh": {"per_query": selected / per_q, "original_union": orig_pages / per_q,
-                                     "affinity_union": total_pages / per_q},
-            "masked_slot_frac": (slots - selected) / slots if slots else 0.0,
+                                     "affinity_union": group_pages / per_q,
+                                     "streamed": total_pages / per_q},
+            "execution": "two halves per group, each over its own union" if halves else "whole groups",
+            "masked_slot_frac": st_group["masked_frac"],
+            "masked_slot_frac_streamed": (slots - selected) / slots if slots else 0.0,
             "selected_edges": selected,
         })
 
@@ -529,26 +550,28 @@ def main():
                 "prep_ms": t_arr_prep, "attn_ms": t_arr_attn, "attn_ms_pick_order": t_fixed}
             del arr
 
-        # Wide groups (items of more than 32 rows, the two-wave form) run as two halves, each
-        # over the union of its own members' pages: the same outputs bit for bit.
-        if cfg.g * cfg.max_group > 32 and cfg.max_group % 2 == 0:
-            hv = pw.SparsePrefill(nq=cfg.nq, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, n_pages=cfg.n_pages,
+        # Wide groups (more than 32 query-head rows) run as two halves by default, each half
+        # over the union of its own members' pages; the whole-group execution (the two-wave
+        # form over the group's union) is timed beside it: the same outputs bit for bit.
+        if plan.halves:
+            wh = pw.SparsePrefill(nq=cfg.nq, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, n_pages=cfg.n_pages,
                                   page_size=cfg.ps, kv_len=cfg.kv_len, k=ids.shape[2], window=cfg.window,
-                                  max_group=cfg.max_group, halves=True, device=dev)
-            out_hv = torch.empty_like(q)
-            t_hv_prep = timed(lambda: hv.prepare(ids, stream))
+                                  max_group=cfg.max_group, halves=False, device=dev)
+            out_wh = torch.empty_like(q)
+            t_wh_prep = timed(lambda: wh.prepare(ids, stream))
             for _ in range(30):   # (a form not run so far: settle it before timing)
-                hv.attend(q, kc, vc, q_pos, out_hv, ks, vs, stream=stream)
-            t_hv_attn = timed(lambda: hv.attend(q, kc, vc, q_pos, out_hv, ks, vs, stream=stream), n=30)
-            plan.attend(q, kc, vc, q_pos, out, ks, vs, stream=stream)   # whole groups, again
+                wh.attend(q, kc, vc, q_pos, out_wh, ks, vs, stream=stream)
+            t_wh_attn = timed(lambda: wh.attend(q, kc, vc, q_pos, out_wh, ks, vs, stream=stream), n=30)
             torch.cuda.synchronize()
-            extras["half_groups"] = {
-                "prep_ms": t_hv_prep, "attn_ms": t_hv_attn, "call_ms": t_hv_prep + t_hv_attn,
-                "queries_per_s": cfg.nq / ((t_hv_prep + t_hv_attn) / 1e3),
-                "union_pages": int(hv.union_off[-1].item()), "union_pages_whole_groups": total_pages,
-                "attn_ms_whole_groups": t_fixed,
-                "bit_identical": bool(torch.equal(out_hv.view(torch.int16), out.view(torch.int16)))}
-            del hv, out_hv
+            wh_pages = int(wh.union_off[-1].item())
+            extras["whole_groups"] = {
+                "prep_ms": t_wh_prep, "attn_ms": t_wh_attn, "call_ms": t_wh_prep + t_wh_attn,
+                "queries_per_s": cfg.nq / ((t_wh_prep + t_wh_attn) / 1e3),
+                "union_pages": wh_pages, "union_pages_halves": total_pages,
+                "union_bytes": unique_kv_bytes(wh_pages, cfg),
+                "attn_ms_halves": t_fixed,
+                "bit_identical": bool(torch.equal(out_wh.view(torch.int16), out.view(torch.int16)))}
+            del wh, out_wh
 
         # The direct KV-page union on the same inputs: every (KV head, page) once,
         # per-page partials, lse merge (a separate entry point, compared here).

@@ -31,7 +31,8 @@ def device_inputs(w, dev="cuda"):
     return d
 
 
-def make_plan(w, grouping="affinity", window=None, max_group=None, dev="cuda", fused=True, arrange=False):
+def make_plan(w, grouping="affinity", window=None, max_group=None, dev="cuda", fused=True, arrange=False,
+              halves=False):
     c = w.cfg
     ids = w.topk if w.topk is not None else w.mask_rows
     mode = "topk" if w.topk is not None else "block_union"
@@ -41,13 +42,13 @@ def make_plan(w, grouping="affinity", window=None, max_group=None, dev="cuda", f
                             kv_len=c.kv_len, k=ids.shape[2], window=window or c.window,
                             max_group=max_group or c.max_group, mode=mode, grouping=grouping,
                             n_rows=ids.shape[0] if mode == "block_union" else 0, fused=fused,
-                            arrange=arrange, device=dev)
+                            arrange=arrange, halves=halves if mode == "topk" else False, device=dev)
 
 
 def run_gpu(w, grouping="affinity", window=None, max_group=None, with_lse=True, fused=True,
-            arrange=False):
+            arrange=False, halves=False):
     d = device_inputs(w)
-    plan = make_plan(w, grouping, window, max_group, fused=fused, arrange=arrange)
+    plan = make_plan(w, grouping, window, max_group, fused=fused, arrange=arrange, halves=halves)
     out = torch.full_like(d["q"], float("nan"))
     lse = torch.full(d["q"].shape[:2], float("nan"), dtype=torch.float32, device="cuda") if with_lse else None
     plan(d["ids"], d["q"], d["k"], d["v"], d["q_pos"], out, d["k_scale"], d["v_scale"], lse)

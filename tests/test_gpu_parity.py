@@ -48,6 +48,19 @@ def test_workload_parity(name):
     check_lse(res["lse"], L, name)
     print(f"[parity] {name}: rows={cfg.nq * cfg.hq} max_abs={mx:.3e} mean_abs={mean:.3e} nrms={nrms:.3f}%",
           flush=True)
+    if w.topk is not None and cfg.g * cfg.max_group > 32:
+        # the default plan runs these wide groups as two halves over their own unions: the
+        # halves' tables are the oracle's unions of each half, and every output and lse bit
+        # equals the whole-group run checked above
+        hv, plan = run_gpu(w, halves=True)
+        assert plan.halves
+        half = [[h for m in grp for h in (m[:cfg.max_group // 2], m[cfg.max_group // 2:])]
+                for grp in ref["groups"]]
+        off, pages, qmask = prep.union_tables(prep.page_bitsets(w.topk, cfg.n_pages), half)
+        assert np.array_equal(hv["union_off"], off)
+        assert np.array_equal(hv["union_pages"], pages)
+        assert np.array_equal(hv["union_qmask"], qmask)
+        assert np.array_equal(hv["out"], res["out"]) and np.array_equal(hv["lse"], res["lse"])
 
 
 def _small(**kw):
