@@ -7,10 +7,15 @@ Hq=32, Hkv=8, d=128, 64-token pages, Top16 per (query, KV head), OCP e4m3 KV
 with per-page fp32 scales).  Inputs are resident in HBM before timing starts.
 
 Prints one JSON line.  ``roofline`` refers to the attention kernel (the
-dominant one): achieved = unique-KV bytes (every group's union pages, K and V
-plus their scales) / the kernel's mean duration from HIP events on its own
-stream.  ``cpu_baseline`` times the CPU oracle on a bounded sample (the first
-windows of the chunk), single-threaded.
+dominant one, timed live with HIP events on its own stream) as a hierarchical
+roofline: each level's traffic or work over that level's peak - L2 (the
+algorithmic bytes through it against a measured L2-resident read of the same
+load path), HBM (calibrated FETCH/WRITE counters), MFMA (MOPS counters against
+the dense peaks) and VALU (issue cycles) - and ``bound`` names the level with
+the largest fraction.  The counters come from the committed rocprofv3 summary
+of the same kernel source (profiles/).  ``cpu_baseline`` times the CPU oracle
+(route A, every row of the chunk, on the host's cores), and ``extra.accuracy``
+compares the timed output with it.
 """
 from __future__ import annotations
 
@@ -277,23 +282,41 @@ def read_peaks(dev, reps: int = 5) -> dict:
     return out
 
 
-def roofline_levels(Bu: float, t_attn_s: float, ctr, peaks) -> dict:
-    """The attention kernel against each resource that could bound it.
-      logical: the union bytes B_u (every group's union read once) over the kernel time,
-               against the 8 TB/s HBM peak - not a bound: the re-reads of pages that other
-               groups also read come from the caches, so this may exceed 1;
+def roofline_levels(Bu: float, qo_bytes: float, t_attn_s: float, ctr, peaks) -> dict:
+    """The attention kernel against each resource that could bound it (a hierarchical
+    roofline: each level's traffic over that level's peak).
+      l2:      the algorithmic bytes that pass through the L2 - every group's union tiles once
+               (B_u) plus the Q rows read and the output rows written - over the kernel time,
+               against the measured read rate of a plain streaming read of an L2-resident
+               buffer through the same direct-to-LDS load path (cross-checked against the
+               counter-measured L2 requests, TCC_REQ x 128 B);
       hbm:     counter-measured bytes between the L2 and memory (FETCH_SIZE + WRITE_SIZE,
                calibrated) against 8 TB/s;
       mfma:    counter-measured MFMA work (MOPS) as the time the matrix cores need at their
-               dense peak (bf16 2.5, fp8 5.0 PFLOP/s) over the kernel time;
-      valu:    counter-measured vector-ALU issue cycles over the kernel's SIMD cycles;
-      cache:   B_u over the kernel time against the measured read rate of a plain
-               streaming read of the level that serves it (the L2 hit fraction h from the
-               counters: 1 / (h / L2 rate + (1 - h) / last-level rate), with the
-               direct-to-LDS load path's rates)."""
-    lv = {"logical": {"achieved": Bu / t_attn_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                      "frac": Bu / t_attn_s / 1e9 / HBM_PEAK_GBS, "bound": False,
-                      "what": "union bytes B_u / kernel time vs HBM peak (not a bound: cache-served re-reads)"}}
+               dense peaks (bf16 2.5, fp8 5.0 PFLOP/s) over the kernel time;
+      valu:    counter-measured vector-ALU issue cycles over the kernel's SIMD cycles.
+    Not bounds (reported for reference): `logical` = the union bytes B_u over the kernel
+    time against the 8 TB/s HBM peak (re-reads of pages other groups also read come from
+    the L2, so this exceeds 1), and `llc` = B_u against the measured read rate of a buffer
+    resident in the 256 MB last-level cache (also exceeded: most of B_u is served by L2)."""
+    ach = Bu / t_attn_s / 1e9
+    lv = {"logical": {"achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                      "bound": False, "what": "union bytes B_u / kernel time vs HBM peak (not a bound)"}}
+    if peaks:
+        p_llc = peaks["mall"]["lds_GBs"]
+        lv["llc"] = {"achieved": ach, "peak": p_llc, "unit": "GB/s", "frac": ach / p_llc, "bound": False,
+                     "what": "B_u / kernel time vs a measured last-level-cache-resident read (not a bound: L2 "
+                             "serves most of B_u)"}
+    if peaks:
+        l2b = Bu + qo_bytes
+        p_l2 = peaks["l2"]["lds_GBs"]
+        lv["l2"] = {"achieved": l2b / t_attn_s / 1e9, "peak": p_l2, "unit": "GB/s",
+                    "frac": l2b / t_attn_s / 1e9 / p_l2, "bytes_per_launch": l2b,
+                    "what": "(B_u + Q + O bytes) per launch / kernel time vs the measured L2-resident read "
+                            "rate of the direct-to-LDS load path"}
+        if ctr and ctr.get("l2_requests"):
+            lv["l2"]["counter_bytes_per_launch"] = ctr["l2_requests"] * 128.0
+            lv["l2"]["l2_hit"] = ctr.get("l2_hit")
     if ctr:
         hb = ctr["fetch_bytes"] + ctr["write_bytes"]
         lv["hbm"] = {"achieved": hb / t_attn_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -305,19 +328,10 @@ def roofline_levels(Bu: float, t_attn_s: float, ctr, peaks) -> dict:
                       "peak": (fb + f8) / t_peak / 1e12 if t_peak else MFMA_PEAK_FLOPS["bf16"] / 1e12,
                       "unit": "TFLOP/s", "frac": t_peak / t_attn_s, "flops_per_launch": fb + f8,
                       "flops_bf16": fb, "flops_fp8": f8,
-                      "what": "MFMA MOPS x 512 per launch; peak = dtype-weighted dense peak"}
+                      "what": "MFMA MOPS x 512 per launch; peak = the dtype-weighted dense peak"}
         if ctr.get("valu_busy") is not None:
             lv["valu"] = {"achieved": ctr["valu_busy"], "peak": 1.0, "unit": "fraction of SIMD cycles",
                           "frac": ctr["valu_busy"], "what": "vector-ALU issue cycles / SIMD cycles (counters)"}
-        h = ctr.get("l2_hit")
-        if peaks and h is not None:
-            p_l2, p_llc = peaks["l2"]["lds_GBs"], peaks["mall"]["lds_GBs"]
-            p_eff = 1.0 / (h / p_l2 + (1.0 - h) / p_llc)
-            lv["cache"] = {"achieved": Bu / t_attn_s / 1e9, "peak": p_eff, "unit": "GB/s",
-                           "frac": Bu / t_attn_s / 1e9 / p_eff, "l2_hit": h,
-                           "l2_read_GBs": p_l2, "llc_read_GBs": p_llc,
-                           "what": "B_u / kernel time vs measured L2 / last-level read rates, "
-                                   "weighted by the counter-measured L2 hit fraction"}
     return lv
 
 
@@ -751,8 +765,9 @@ def main():
     peaks = read_peaks(dev)
     extras["read_peaks_GBs"] = peaks
     ctr = profiled_counters(cfg.name)
-    levels = roofline_levels(Bu, attn_ms / 1e3, ctr, peaks)
-    bounds = {k: v for k, v in levels.items() if k != "logical"}
+    qo_bytes = 2.0 * cfg.nq * cfg.hq * cfg.d * 2                    # Q read and O written, bf16
+    levels = roofline_levels(Bu, qo_bytes, attn_ms / 1e3, ctr, peaks)
+    bounds = {k: v for k, v in levels.items() if v.get("bound", True)}
     bound = max(bounds, key=lambda k: bounds[k]["frac"]) if bounds else "logical"
     top = levels[bound]
     if ctr:
@@ -761,8 +776,8 @@ def main():
                               "frac_at_profiled_time": {k: v["frac"] * attn_ms * 1e3 / ctr["mean_us"]
                                                         for k, v in bounds.items() if ctr.get("mean_us")}}
     else:
-        levels["counters"] = {"source": None, "note": "no counters for this kernel source: only the "
-                                                      "logical and measured-cache levels are known"}
+        levels["counters"] = {"source": None, "note": "no counters for this kernel source: the hbm, mfma "
+                                                      "and valu levels are unknown"}
 
     # arithmetic of the attention's MFMAs: fp8 KV with d = 128 takes QK on the fp8 MFMA
     dtype = "fp8/bf16" if cfg.kv_dtype == "fp8" and cfg.d == 128 else "bf16"
