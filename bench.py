@@ -6,6 +6,13 @@ default workload is the long-context fp8 case (64K context, 4096-query chunk,
 Hq=32, Hkv=8, d=128, 64-token pages, Top16 per (query, KV head), OCP e4m3 KV
 with per-page fp32 scales).  Inputs are resident in HBM before timing starts.
 
+Warm-up: the W calls of ``--warmup``, then untimed calls until the warm-up has
+lasted ``--settle-ms`` of wall time (100 ms).  After the GPU has been idle the time
+of a call moves over the first ~30 ms of steady work (C3 attention: about 0.35 ms,
+then up to 0.40 ms, then 0.30 ms from the ~75th call on), so a count of calls alone
+leaves short warm-ups inside that transient.  The K calls right after the W warm-up
+calls are timed as well and reported as ``extra.warmup.right_after_warmup``.
+
 Prints one JSON line.  ``roofline`` refers to the attention kernel (the
 dominant one, timed live with HIP events on its own stream) as a hierarchical
 roofline: each level's traffic or work over that level's peak - L2 (the
@@ -43,6 +50,11 @@ def parse():
     # the chip's clocks take some tens of milliseconds of steady work to settle: 200 untimed
     # calls of the 64K fp8 Top16 workload are about 80 ms
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="after the --warmup calls, more untimed calls until the warm-up has lasted this "
+                         "long (wall time): after idle the per-call time moves for about 30 ms of steady "
+                         "work before it settles; the K calls right after the W warm-up calls are timed "
+                         "too and reported as extra.right_after_warmup")
     ap.add_argument("--workload", default="c3_long_fp8")
     ap.add_argument("--window", type=int, default=None)
     ap.add_argument("--item-rows", type=int, default=None,
@@ -294,7 +306,13 @@ def roofline_levels(Bu: float, qo_bytes: float, t_attn_s: float, ctr, peaks) -> 
                calibrated) against 8 TB/s;
       mfma:    counter-measured MFMA work (MOPS) as the time the matrix cores need at their
                dense peaks (bf16 2.5, fp8 5.0 PFLOP/s) over the kernel time;
-      valu:    counter-measured vector-ALU issue cycles over the kernel's SIMD cycles.
+      valu:    counter-measured vector-ALU issue cycles over the kernel's SIMD cycles;
+      simd:    vector-ALU issue cycles plus MFMA busy cycles over the SIMD cycles: the two
+               pipes as one wave's dependent chain uses them (QK on MFMA -> softmax on the
+               VALU -> PV on MFMA), which two waves per SIMD overlap only in part (an MFMA's
+               issue cycle is counted in both terms: at most 0.05 on these kernels).
+    The counter fractions are taken over the profiled launches and rescaled to the live kernel
+    time (same cycles of work in the live duration).
     Not bounds (reported for reference): `logical` = the union bytes B_u over the kernel
     time against the 8 TB/s HBM peak (re-reads of pages other groups also read come from
     the L2, so this exceeds 1), and `llc` = B_u against the measured read rate of a buffer
@@ -329,9 +347,15 @@ def roofline_levels(Bu: float, qo_bytes: float, t_attn_s: float, ctr, peaks) -> 
                       "unit": "TFLOP/s", "frac": t_peak / t_attn_s, "flops_per_launch": fb + f8,
                       "flops_bf16": fb, "flops_fp8": f8,
                       "what": "MFMA MOPS x 512 per launch; peak = the dtype-weighted dense peak"}
+        scale = ctr["mean_us"] / (t_attn_s * 1e6) if ctr.get("mean_us") else 1.0
         if ctr.get("valu_busy") is not None:
-            lv["valu"] = {"achieved": ctr["valu_busy"], "peak": 1.0, "unit": "fraction of SIMD cycles",
-                          "frac": ctr["valu_busy"], "what": "vector-ALU issue cycles / SIMD cycles (counters)"}
+            v = ctr["valu_busy"] * scale
+            lv["valu"] = {"achieved": v, "peak": 1.0, "unit": "fraction of SIMD cycles", "frac": v,
+                          "what": "vector-ALU issue cycles / SIMD cycles (counters)"}
+            if ctr.get("mfma_busy") is not None:
+                sm = (ctr["valu_busy"] + ctr["mfma_busy"]) * scale
+                lv["simd"] = {"achieved": sm, "peak": 1.0, "unit": "fraction of SIMD cycles", "frac": sm,
+                              "what": "(vector-ALU issue + MFMA busy cycles) / SIMD cycles (counters)"}
     return lv
 
 
@@ -414,9 +438,24 @@ def main():
                           "path": args.profile_path}))
         return
 
+    t_warm = time.perf_counter()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # the same K calls timed right after the W warm-up calls (with few warm-up calls the GPU is
+    # still leaving its idle state), then untimed calls until the warm-up has lasted settle_ms
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    first_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    settle_calls = 0
+    while (time.perf_counter() - t_warm) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            step()
+        settle_calls += 10
+        torch.cuda.synchronize()
+    warm_wall_ms = (time.perf_counter() - t_warm) * 1e3
 
     # ---- the timed region: K complete steps back to back -------------------------------
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -431,6 +470,9 @@ def main():
     t_attn = [evs[i][1].elapsed_time(evs[i][2]) for i in range(args.steps)]
     ms_step = wall * 1e3 / args.steps
     value = cfg.nq / (ms_step / 1e3)
+    settle = {"warmup_calls": args.warmup, "right_after_warmup_calls": args.steps,
+              "settle_calls": settle_calls, "untimed_wall_ms": warm_wall_ms, "settle_ms": args.settle_ms,
+              "right_after_warmup": {"ms_per_step": first_ms, "queries_per_s": cfg.nq / (first_ms / 1e3)}}
 
     def timed(fn, n=10):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -455,7 +497,7 @@ def main():
     extras = {"t_prep_ms_mean": statistics.mean(t_prep), "t_attn_ms_mean": attn_ms,
               "t_attn_ms_median": statistics.median(t_attn), "union_pages": total_pages,
               "page_visits": visits,
-              "unique_kv_bytes": Bu}
+              "unique_kv_bytes": Bu, "warmup": settle}
     n_items = len(off) - 1 if mode == "topk" else cfg.hkv * plan.n_groups
     halves = mode == "topk" and plan.halves
     members = item_members((plan.half_qids if halves else plan.group_qids).cpu().numpy()

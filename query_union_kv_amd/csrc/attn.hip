@@ -713,10 +713,16 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
         if constexpr (C::kStreamK) {
           s2[kb] = s2all[m][kb];
         } else if constexpr (!C::kF8Mma) {   // (the held fp8 form computed S above)
+          // one-row-tile waves (two of them share an item's ring) raise their priority
+          // while they issue MFMAs, so that a wave entering its MFMA block goes ahead of
+          // one in its softmax and the two drift into alternating phases (C2 attention
+          // 0.143 -> 0.137 ms; the two-row-tile forms gain nothing from it)
+          if constexpr (MT == 1) if (kb == 0) __builtin_amdgcn_s_setprio(1);
           s2[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int c = 0; c < C::kDc; ++c)
             s2[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][c], qf[m][c], s2[kb], 0, 0, 0);
+          if constexpr (MT == 1) if (kb == 1) __builtin_amdgcn_s_setprio(0);
         }
       }
       // lane holds row li of tile m and tile keys 8*lq + 4*kb + ii
@@ -804,6 +810,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     // MFMAs form one block behind one uniform branch, and an inactive row tile (P = 0)
     // skips its block; otherwise every row tile runs (its P is 0 when inactive).
     if constexpr (kEarlyV) {
+      if constexpr (MT == 1) __builtin_amdgcn_s_setprio(1);   // (see the QK block above)
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (MT > 1 && !act[m]) continue;
@@ -811,6 +818,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
         for (int dt = 0; dt < C::kDt; ++dt)
           o[m][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pf[m], o[m][dt], 0, 0, 0);
       }
+      if constexpr (MT == 1) __builtin_amdgcn_s_setprio(0);
     } else {
 #pragma unroll
       for (int dt = 0; dt < C::kDt; ++dt) {

@@ -71,3 +71,28 @@ def test_row_tile_work_rule():
     r = bench.row_tile_work(off, pages, None, members, np.array([90, 10]), 8, 64, 1000,
                             shared_table=True)
     assert r["active_pairs"] == 3                                       # the tile at token 96 > 90 is skipped
+
+
+def test_roofline_levels_follow_the_committed_counters():
+    """With the live kernel time equal to the profiled mean, every counter level reproduces the
+    per-launch figures of the committed summary: bytes / mean duration / peak, and the busy
+    fractions as measured; at twice the time every fraction halves."""
+    ctr = bench.profiled_counters("c3_long_fp8")
+    if ctr is None:   # the summary was taken with another attention source
+        import pytest
+        pytest.skip("profiles/k_attn_c3_long_fp8.md does not match the attention source")
+    peaks = {"l2": {"lds_GBs": 29000.0}, "mall": {"lds_GBs": 7000.0}}
+    t = ctr["mean_us"] * 1e-6
+    Bu, qo = 6.0e9, 1.0e8
+    lv = bench.roofline_levels(Bu, qo, t, ctr, peaks)
+    hb = ctr["fetch_bytes"] + ctr["write_bytes"]
+    assert abs(lv["hbm"]["frac"] - hb / t / 8e12) < 1e-12
+    assert abs(lv["l2"]["frac"] - (Bu + qo) / t / 29000e9) < 1e-12
+    assert abs(lv["valu"]["frac"] - ctr["valu_busy"]) < 1e-12
+    assert abs(lv["simd"]["frac"] - (ctr["valu_busy"] + ctr["mfma_busy"])) < 1e-12
+    t_mfma = (ctr["mops_bf16"] * 512 / 2.5e15) + (ctr["mops_f8"] * 512 / 5.0e15)
+    assert abs(lv["mfma"]["frac"] - t_mfma / t) < 1e-12
+    assert lv["logical"]["bound"] is False and lv["llc"]["bound"] is False
+    lv2 = bench.roofline_levels(Bu, qo, 2 * t, ctr, peaks)
+    for k in ("hbm", "l2", "valu", "simd", "mfma"):
+        assert abs(lv2[k]["frac"] - lv[k]["frac"] / 2) < 1e-12, k
