@@ -528,7 +528,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
 
   // ---- running state ------------------------------------------------------------------
   f32x4 o[MT][C::kDt];
-  float m_ref[MT], l_run[MT];
+  float m_ref[MT], l_run[MT], thr[MT];   // thr: rescale threshold of the row-sum share (below)
   int mt_min[MT];   // smallest usable last token over the valid rows of a row tile
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
@@ -536,6 +536,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     for (int dt = 0; dt < C::kDt; ++dt) o[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_ref[m] = -INFINITY;
     l_run[m] = 0.f;
+    thr[m] = -INFINITY;
     int lim = my_bit[m] != 0 ? row_lim[m] : 0x7fffffff;   // my_bit != 0: the row has a query
 #pragma unroll
     for (int sh = 1; sh < 16; sh <<= 1) lim = min(lim, __shfl_xor(lim, sh, kWave));
@@ -566,6 +567,12 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
   struct PageCtx {
     int pg, qm, abits;        // page (-1: invalid), member mask, bit m: row tile m selects it
     float sc, lvs, inv_vs;    // score scale * ks, log2 vs, 1 / vs
+    // per selecting row tile m (bit m of abits): the row's score scale, the bias of the
+    // fast-path exponent (log2 vs - reference, or -inf for a row that did not select the page
+    // or has no reference yet; kept current when a rescale moves the reference), and the
+    // lanes whose row selected the page
+    float scm[MT], bias[MT];
+    uint64_t selm[MT];
   };
   auto page_ctx = [&](int t) {
     const int ent = t >> tpp_shift;
@@ -583,10 +590,22 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     c.sc = lane_f(md_sc, l);
     c.lvs = lane_f(md_lvs, l);
     c.inv_vs = lane_f(md_ivs, l);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      c.scm[m] = 0.f;
+      c.bias[m] = -INFINITY;
+      c.selm[m] = 0;
+      if ((c.abits >> m) & 1) {   // uniform
+        const bool sel = (c.qm & my_bit[m]) != 0;
+        c.scm[m] = C::kF8Mma ? c.sc * qs[m] : c.sc;   // fp8 MFMA: undo the row's 2^e
+        c.bias[m] = sel && m_ref[m] != -INFINITY ? c.lvs - m_ref[m] : -INFINITY;
+        c.selm[m] = __builtin_amdgcn_ballot_w64(sel);
+      }
+    }
     return c;
   };
 
-  auto compute = [&](int t, auto stage_c, const PageCtx& pc) {
+  auto compute = [&](int t, auto stage_c, PageCtx& pc) {
     constexpr int SS = decltype(stage_c)::value;
     const int pg = pc.pg, qm = pc.qm;
     const int tok0 = pg * p.page_size + (t & ((1 << tpp_shift) - 1)) * kTK;
@@ -726,9 +745,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
         }
       }
       // lane holds row li of tile m and tile keys 8*lq + 4*kb + ii
-      const float scm = C::kF8Mma ? sc * qs[m] : sc;   // fp8 MFMA: undo the row's 2^e
-      const bool sel = (qm & my_bit[m]) != 0;
-      const bool row_any = sel && tok0 <= row_lim[m];
+      const float scm = pc.scm[m];
       const bool tile_full = tok0 + kTK - 1 <= mt_min[m];          // uniform
       // scores in the log2 domain; keys after a row's last usable token -> -inf.  A tile
       // wholly before every row's limit (the common case) needs no causal compare.
@@ -747,7 +764,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       };
       // fast path: P = exp2(s*sc - reference + log2 vs) with the current reference
       float pv[8];
-      const float bias0 = sel && m_ref[m] != -INFINITY ? lvs - m_ref[m] : -INFINITY;
+      const float bias0 = pc.bias[m];
       if (tile_full)
         scores(bias0, pv, std::false_type{});
       else
@@ -775,10 +792,13 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       // row sum passed 2^30, or overflowed): rare, wave-uniform slow path.  The decision is
       // made per row - lanes li, li+16, li+32 and li+48 hold row li - so that every key of
       // a row is exponentiated against the same reference.
-      // (bitwise, not short-circuit: straight-line compares instead of exec-mask branches)
-      const bool need_lane = row_any & ((m_ref[m] == -INFINITY) | !(lsum * inv_vs <= kRescaleShare));
-      const uint64_t nb = __builtin_amdgcn_ballot_w64(need_lane);
+      // A lane needs it when its row selected the page and reaches into the tile, and its
+      // share of the row sum is above thr (-inf while the row has no reference, else 2^30;
+      // the row sum is never negative, so this is "no reference yet, or above 2^30").
+      uint64_t nb = __builtin_amdgcn_ballot_w64(!(lsum * inv_vs <= thr[m])) & pc.selm[m];
+      if (!tile_full) nb &= __builtin_amdgcn_ballot_w64(tok0 <= row_lim[m]);
       if (nb) {
+        const bool sel = (qm & my_bit[m]) != 0;
         const uint32_t rows = (uint32_t)(nb | (nb >> 16) | (nb >> 32) | (nb >> 48)) & 0xFFFFu;
         const bool need = (rows >> li) & 1u;
         float raw[8];
@@ -794,12 +814,13 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
 #pragma unroll
         for (int dt = 0; dt < C::kDt; ++dt) o[m][dt] *= alpha;
         m_ref[m] = m_new;
+        thr[m] = m_new == -INFINITY ? -INFINITY : kRescaleShare;
+        pc.bias[m] = (sel && m_new != -INFINITY) ? lvs - m_new : -INFINITY;   // (the page's next tile)
         // only the rows that moved their reference recompute P: every other row keeps its
         // fast-path values, so a row's arithmetic never depends on its tile-mates
         if (need) {
-          const float bias = (sel && m_new != -INFINITY) ? lvs - m_new : -INFINITY;
 #pragma unroll
-          for (int k = 0; k < 8; ++k) pv[k] = __builtin_amdgcn_exp2f(raw[k] + bias);
+          for (int k = 0; k < 8; ++k) pv[k] = __builtin_amdgcn_exp2f(raw[k] + pc.bias[m]);
           lsum = round_sum(pv, pf[m]);
         }
       }
@@ -832,7 +853,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
 
   // ---- pipeline: tile t lives in stage t % ST; the loop is unrolled by ST so that every
   // stage offset is a compile-time immediate ------------------------------------------------
-  auto step = [&](int t, auto stage_c, const PageCtx& pc, int pg_next) {
+  auto step = [&](int t, auto stage_c, PageCtx& pc, int pg_next) {
     constexpr int SS = decltype(stage_c)::value;
     wait_tiles<C::kDmaPerTile, ST - 2>(min(n_tiles - 1 - t, ST - 2));   // tile t has landed
     if constexpr (NW > 1) __builtin_amdgcn_s_barrier();                 // ... for every wave
@@ -849,8 +870,14 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     __builtin_amdgcn_s_barrier();      // ... and every other wave's
     if (t + 2 < n_tiles) issue(t + 2, sc, kNoPage);
     if (t + 3 < n_tiles) issue(t + 3, sd, kNoPage);
-    compute(t, sa, page_ctx(t));
-    if (t + 1 < n_tiles) compute(t + 1, sb, page_ctx(t + 1));
+    {
+      PageCtx c = page_ctx(t);
+      compute(t, sa, c);
+    }
+    if (t + 1 < n_tiles) {   // (its page values read after tile t's rescale, if any)
+      PageCtx c = page_ctx(t + 1);
+      compute(t + 1, sb, c);
+    }
   };
   if (0 < n_tiles) issue(0, std::integral_constant<int, 0>{}, kNoPage);
   if constexpr (ST > 2) if (1 < n_tiles) issue(1, std::integral_constant<int, 1>{}, kNoPage);
@@ -868,18 +895,31 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     // a page holds 2 or 4 tiles and t0 is even, so tiles t0 and t0 + 1 share a page: its
     // values are read once, and the load of tile t0 + 1 needs no page lookup
     for (int t0 = 0; t0 < n_tiles; t0 += 2) {
-      const PageCtx pc = page_ctx(t0);
+      PageCtx pc = page_ctx(t0);   // (a rescale in tile t0 updates its bias for t0 + 1)
       step(t0, std::integral_constant<int, 0>{}, pc, pc.pg);
       if (t0 + 1 < n_tiles) step(t0 + 1, std::integral_constant<int, 1>{}, pc, kNoPage);
     }
   } else {
     for (int t0 = 0; t0 < n_tiles; t0 += ST) {
-      step(t0, std::integral_constant<int, 0>{}, page_ctx(t0), kNoPage);
-      if (t0 + 1 < n_tiles) step(t0 + 1, std::integral_constant<int, 1>{}, page_ctx(t0 + 1), kNoPage);
+      // (each tile's page values are read after the previous tile's rescale, if any)
+      {
+        PageCtx c = page_ctx(t0);
+        step(t0, std::integral_constant<int, 0>{}, c, kNoPage);
+      }
+      if (t0 + 1 < n_tiles) {
+        PageCtx c = page_ctx(t0 + 1);
+        step(t0 + 1, std::integral_constant<int, 1>{}, c, kNoPage);
+      }
       if constexpr (ST > 2)
-        if (t0 + 2 < n_tiles) step(t0 + 2, std::integral_constant<int, 2>{}, page_ctx(t0 + 2), kNoPage);
+        if (t0 + 2 < n_tiles) {
+          PageCtx c = page_ctx(t0 + 2);
+          step(t0 + 2, std::integral_constant<int, 2>{}, c, kNoPage);
+        }
       if constexpr (ST > 3)
-        if (t0 + 3 < n_tiles) step(t0 + 3, std::integral_constant<int, 3>{}, page_ctx(t0 + 3), kNoPage);
+        if (t0 + 3 < n_tiles) {
+          PageCtx c = page_ctx(t0 + 3);
+          step(t0 + 3, std::integral_constant<int, 3>{}, c, kNoPage);
+        }
     }
   }
   wait_vmcnt<0>();
