@@ -204,6 +204,24 @@ pw_status pw_prepare(const int32_t* topk, int nq, int hkv, int k, int n_pages, i
                      uint8_t* union_qmask, int64_t capacity, int32_t* item_order,
                      hipStream_t stream);
 
+/* The same for groups run as two halves (QUILT summary, "Cascaded Sharing": the subgroup
+ * level of the sharing cascade): bitsets and groups exactly as pw_prepare, then the union
+ * tables of each group's two halves instead of the group's - exactly
+ * pw_union_tables(bits, group_rows = group_qids viewed as [hkv][2G][max_group/2],
+ * group_size = NULL, n_groups = 2G, group_width = max_group/2, k_max = k, union_qmask):
+ * table 2j + h lists the union of members [h*max_group/2, (h+1)*max_group/2) of group j
+ * in pick order (absent members are -1 and skipped), with their member masks.  Run the
+ * attention on these tables with group_qids viewed the same way, n_groups = 2G and
+ * max_group/2 members per table.  max_group must be even; capacity >=
+ * pw_union_capacity(2*hkv*G, max_group/2, k, n_pages); item_order, when given, has 2*hkv*G
+ * entries (pw_schedule_items over the half tables).  Same fused launches as pw_prepare
+ * for window <= 64 and n_pages <= 1024.                                                */
+pw_status pw_prepare_halves(const int32_t* topk, int nq, int hkv, int k, int n_pages, int window,
+                            int max_group, uint64_t* bits, int32_t* bad_id_count,
+                            int32_t* group_qids, int32_t* group_size, int32_t* union_off,
+                            int32_t* union_pages, uint8_t* union_qmask, int64_t capacity,
+                            int32_t* item_order, hipStream_t stream);
+
 /* ---- (4) ID-aware union attention -----------------------------------------------------
  * PageWeaver abstract, Fig. 1 and Fig. 3: each group's union pages are staged
  * on chip once; for every member the same lanes compute QK, the masked online

@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
             "pw_union_tables": (I, [P, I, I, I, P, P, I, I, I, P, P, P, I64, P]),
             "pw_arrange_groups": (I, [P, I, I, I, I, I, I, P, P, P, P, I64, P]),
             "pw_prepare": (I, [P, I, I, I, I, I, I, P, P, P, P, P, P, P, I64, P, P]),
+            "pw_prepare_halves": (I, [P, I, I, I, I, I, I, P, P, P, P, P, P, P, I64, P, P]),
             "pw_sparse_prefill": (I, [P, I, I, I, I, P, P, I, P, P, I, I, I64, I64, P, I, F,
                                       P, P, I, I, I, P, P, P, I64, P, P, P, P]),
             "pw_schedule_items": (I, [P, I, P, P]),
@@ -253,20 +254,23 @@ def pw_prepare(topk: torch.Tensor, n_pages: int, window: int, max_group: int,
                bits: torch.Tensor, group_qids: torch.Tensor, group_size: torch.Tensor,
                union_off: torch.Tensor, union_pages: torch.Tensor, union_qmask: torch.Tensor,
                bad_id_count: Optional[torch.Tensor] = None, stream=None,
-               item_order: Optional[torch.Tensor] = None) -> None:
+               item_order: Optional[torch.Tensor] = None, halves: bool = False) -> None:
     """Fused pw_page_bitsets + pw_group + pw_union_tables (same outputs); with item_order,
-    also the work order of pw_schedule_items."""
+    also the work order of pw_schedule_items.  halves=True calls pw_prepare_halves: the
+    tables are those of each group's two halves (2 * hkv * n_groups tables)."""
     nq, hkv, k = topk.shape
     n_groups = pw_num_groups(nq, window, max_group)
-    if item_order is not None and item_order.numel() != hkv * n_groups:
+    n_tables = hkv * n_groups * (2 if halves else 1)
+    if item_order is not None and item_order.numel() != n_tables:
         raise ValueError("item_order must hold one entry per union table")
     if tuple(bits.shape) != (hkv, nq, pw_words(n_pages)):
         raise ValueError("bits shape")
     if tuple(group_qids.shape) != (hkv, n_groups, max_group) or tuple(group_size.shape) != (hkv, n_groups):
         raise ValueError("group_qids/group_size shapes do not match pw_num_groups")
-    if union_off.numel() != hkv * n_groups + 1 or union_qmask.numel() < union_pages.numel():
+    if union_off.numel() != n_tables + 1 or union_qmask.numel() < union_pages.numel():
         raise ValueError("union table buffer sizes")
-    _check(lib().pw_prepare(_ptr(topk, torch.int32, "topk"), nq, hkv, k, n_pages, window, max_group,
+    fn = lib().pw_prepare_halves if halves else lib().pw_prepare
+    _check(fn(_ptr(topk, torch.int32, "topk"), nq, hkv, k, n_pages, window, max_group,
                             _ptr(bits, torch.int64, "bits"),
                             _ptr(bad_id_count, torch.int32, "bad_id_count"),
                             _ptr(group_qids, torch.int32, "group_qids"),
@@ -603,6 +607,12 @@ class SparsePrefill:
 
     def prepare(self, ids: torch.Tensor, stream=None) -> None:
         """Bitsets, grouping and union tables from topk [nq, hkv, k] or mask rows [n_rows, hkv, k]."""
+        if self.halves and self.grouping == "affinity" and self.fused:
+            # bitsets, groups and the halves' tables (and their work order) in the fused launches
+            pw_prepare(ids, self.n_pages, self.window, self.max_group, self.bits, self.group_qids,
+                       self.group_size, self.union_off, self.union_pages, self.union_qmask,
+                       self.bad_ids, stream, item_order=self.item_order, halves=True)
+            return
         if self.halves:
             pw_page_bitsets(ids, self.n_pages, self.bits, self.bad_ids, stream)
             if self.grouping == "affinity":

@@ -199,50 +199,78 @@ pw_status pw_union_tables(const uint64_t* bits, int n_rows, int hkv, int n_pages
                                  stream);
 }
 
+namespace {
+
+// pw_prepare and pw_prepare_halves: halves = 1 lists the union of each half of every group
+// (tables 2j, 2j + 1 of group j, width max_group / 2) instead of the group's.
+pw_status prepare_common(const char* fn, const int32_t* topk, int nq, int hkv, int k, int n_pages,
+                         int window, int max_group, uint64_t* bits, int32_t* bad_id_count,
+                         int32_t* group_qids, int32_t* group_size, int32_t* union_off,
+                         int32_t* union_pages, uint8_t* union_qmask, int64_t capacity,
+                         int32_t* item_order, int halves, hipStream_t stream) {
+  pw::g_err[0] = 0;
+  if (nq < 0 || hkv < 1 || k < 1 || n_pages < 1)
+    return fail(PW_ERR_ARG, "%s: bad sizes nq=%d hkv=%d k=%d n_pages=%d", fn, nq, hkv, k, n_pages);
+  if (k > 4096) return fail(PW_ERR_UNSUPPORTED, "%s: k=%d > 4096", fn, k);
+  if (max_group < 1 || max_group > 8)
+    return fail(PW_ERR_UNSUPPORTED, "%s: max_group=%d not in 1..8", fn, max_group);
+  if (halves && max_group % 2)
+    return fail(PW_ERR_ARG, "%s: max_group=%d is odd (two halves need an even width)", fn, max_group);
+  if (window < 1 || window > 1024)
+    return fail(PW_ERR_UNSUPPORTED, "%s: window=%d not in 1..1024", fn, window);
+  if (window % max_group)
+    return fail(PW_ERR_ARG, "%s: window=%d is not a multiple of max_group=%d", fn, window, max_group);
+  if (n_pages > 4096) return fail(PW_ERR_UNSUPPORTED, "%s: n_pages=%d > 4096", fn, n_pages);
+  const int n_groups = pw_num_groups(nq, window, max_group);
+  if (n_groups < 0 || (int64_t)n_groups * hkv * max_group > INT32_MAX / 2)
+    return fail(PW_ERR_UNSUPPORTED, "%s: too many groups", fn);
+  const int n_tables = hkv * n_groups * (halves ? 2 : 1);
+  const int width = halves ? max_group / 2 : max_group;
+  const int64_t need = pw_union_capacity(n_tables, width, k, n_pages);
+  if (capacity < need)
+    return fail(PW_ERR_CAPACITY, "%s: capacity %lld < required %lld", fn, (long long)capacity,
+                (long long)need);
+  if (capacity > INT32_MAX)
+    return fail(PW_ERR_UNSUPPORTED, "%s: capacity %lld exceeds int32 offsets", fn, (long long)capacity);
+  if (!union_off) return fail(PW_ERR_ARG, "%s: null union_off", fn);
+  if (nq > 0 && (!topk || !bits || !group_qids || !group_size || !union_pages || !union_qmask))
+    return fail(PW_ERR_ARG, "%s: null pointer argument", fn);
+  if (pw::prepare_fusable(n_pages, window))
+    return pw::launch_prepare(topk, nq, hkv, k, n_pages, window, max_group, n_groups, bits,
+                              bad_id_count, group_qids, group_size, union_off, union_pages,
+                              union_qmask, capacity, item_order, halves, stream);
+  pw_status st = pw::launch_page_bitsets(topk, nq, hkv, k, n_pages, bits, bad_id_count, stream);
+  if (st == PW_OK)
+    st = pw::launch_group(bits, nq, hkv, n_pages, window, max_group, n_groups, group_qids,
+                          group_size, stream);
+  if (st == PW_OK)   // halves: the member lists as [hkv][2 n_groups][mg/2], absent members -1
+    st = pw::launch_union_tables(bits, nq, hkv, n_pages, group_qids, halves ? nullptr : group_size,
+                                 halves ? 2 * n_groups : n_groups, width, union_off, union_pages,
+                                 union_qmask, capacity, stream);
+  if (st == PW_OK && item_order) st = pw::launch_schedule(union_off, n_tables, item_order, stream);
+  return st;
+}
+
+}  // namespace
+
 pw_status pw_prepare(const int32_t* topk, int nq, int hkv, int k, int n_pages, int window,
                      int max_group, uint64_t* bits, int32_t* bad_id_count, int32_t* group_qids,
                      int32_t* group_size, int32_t* union_off, int32_t* union_pages,
                      uint8_t* union_qmask, int64_t capacity, int32_t* item_order,
                      hipStream_t stream) {
-  pw::g_err[0] = 0;
-  if (nq < 0 || hkv < 1 || k < 1 || n_pages < 1)
-    return fail(PW_ERR_ARG, "pw_prepare: bad sizes nq=%d hkv=%d k=%d n_pages=%d", nq, hkv, k, n_pages);
-  if (k > 4096) return fail(PW_ERR_UNSUPPORTED, "pw_prepare: k=%d > 4096", k);
-  if (max_group < 1 || max_group > 8)
-    return fail(PW_ERR_UNSUPPORTED, "pw_prepare: max_group=%d not in 1..8", max_group);
-  if (window < 1 || window > 1024)
-    return fail(PW_ERR_UNSUPPORTED, "pw_prepare: window=%d not in 1..1024", window);
-  if (window % max_group)
-    return fail(PW_ERR_ARG, "pw_prepare: window=%d is not a multiple of max_group=%d", window,
-                max_group);
-  if (n_pages > 4096) return fail(PW_ERR_UNSUPPORTED, "pw_prepare: n_pages=%d > 4096", n_pages);
-  const int n_groups = pw_num_groups(nq, window, max_group);
-  if (n_groups < 0 || (int64_t)n_groups * hkv * max_group > INT32_MAX / 2)
-    return fail(PW_ERR_UNSUPPORTED, "pw_prepare: too many groups");
-  const int64_t need = pw_union_capacity(hkv * n_groups, max_group, k, n_pages);
-  if (capacity < need)
-    return fail(PW_ERR_CAPACITY, "pw_prepare: capacity %lld < required %lld", (long long)capacity,
-                (long long)need);
-  if (capacity > INT32_MAX)
-    return fail(PW_ERR_UNSUPPORTED, "pw_prepare: capacity %lld exceeds int32 offsets",
-                (long long)capacity);
-  if (!union_off) return fail(PW_ERR_ARG, "pw_prepare: null union_off");
-  if (nq > 0 && (!topk || !bits || !group_qids || !group_size || !union_pages || !union_qmask))
-    return fail(PW_ERR_ARG, "pw_prepare: null pointer argument");
-  if (pw::prepare_fusable(n_pages, window))
-    return pw::launch_prepare(topk, nq, hkv, k, n_pages, window, max_group, n_groups, bits,
-                              bad_id_count, group_qids, group_size, union_off, union_pages,
-                              union_qmask, capacity, item_order, stream);
-  pw_status st = pw::launch_page_bitsets(topk, nq, hkv, k, n_pages, bits, bad_id_count, stream);
-  if (st == PW_OK)
-    st = pw::launch_group(bits, nq, hkv, n_pages, window, max_group, n_groups, group_qids,
-                          group_size, stream);
-  if (st == PW_OK)
-    st = pw::launch_union_tables(bits, nq, hkv, n_pages, group_qids, group_size, n_groups,
-                                 max_group, union_off, union_pages, union_qmask, capacity, stream);
-  if (st == PW_OK && item_order)
-    st = pw::launch_schedule(union_off, hkv * n_groups, item_order, stream);
-  return st;
+  return prepare_common("pw_prepare", topk, nq, hkv, k, n_pages, window, max_group, bits,
+                        bad_id_count, group_qids, group_size, union_off, union_pages, union_qmask,
+                        capacity, item_order, 0, stream);
+}
+
+pw_status pw_prepare_halves(const int32_t* topk, int nq, int hkv, int k, int n_pages, int window,
+                            int max_group, uint64_t* bits, int32_t* bad_id_count,
+                            int32_t* group_qids, int32_t* group_size, int32_t* union_off,
+                            int32_t* union_pages, uint8_t* union_qmask, int64_t capacity,
+                            int32_t* item_order, hipStream_t stream) {
+  return prepare_common("pw_prepare_halves", topk, nq, hkv, k, n_pages, window, max_group, bits,
+                        bad_id_count, group_qids, group_size, union_off, union_pages, union_qmask,
+                        capacity, item_order, 1, stream);
 }
 
 int64_t pw_page_items_capacity(int nq, int hkv, int k_max, int n_pages, int chunk) {

@@ -74,7 +74,7 @@ pw_status launch_prepare(const int32_t* topk, int nq, int hkv, int k, int n_page
                          int max_group, int n_groups, uint64_t* bits, int32_t* bad_id_count,
                          int32_t* group_qids, int32_t* group_size, int32_t* union_off,
                          int32_t* union_pages, uint8_t* union_qmask, int64_t capacity,
-                         int32_t* item_order, hipStream_t stream);
+                         int32_t* item_order, int halves, hipStream_t stream);
 
 // Member order of 5..8-member groups for 4-member row tiles, with member-mask bits to match.
 pw_status launch_arrange(const uint64_t* bits, int nq, int hkv, int n_pages, int n_groups,

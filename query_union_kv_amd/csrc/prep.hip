@@ -299,6 +299,10 @@ __global__ __launch_bounds__(64) void k_group_wave(const uint64_t* __restrict__ 
 //    (Measured on the 64K fp8 Top16 tables: one wave per window took 7 us longer and two
 //    waves 11 us longer than four; eight match four there and gain 3 us where a window
 //    spans four words.)
+//  * with `halves` set, each group's two halves - members [0, mg/2) and [mg/2, mg) in pick
+//    order - get a table each (tables 2j and 2j + 1 for group j): the union of the first
+//    half is U as it stood when the half was complete, the second half's union is
+//    accumulated from its own members.
 constexpr int kFusedWordsPerWave = 2;
 constexpr int kFusedMaxWaves = 16 / kFusedWordsPerWave;   // 1024 pages
 static_assert(kFusedMaxWaves == 8, "the partial scores are summed as a tree of eight");
@@ -307,13 +311,13 @@ __global__ __launch_bounds__(64 * kFusedMaxWaves) void k_prepare(
     const int32_t* __restrict__ topk, int nq, int hkv, int k, int n_pages, int words, int window,
     int max_group, int n_groups, uint64_t* __restrict__ bits, int32_t* __restrict__ bad_id_count,
     int32_t* __restrict__ group_qids, int32_t* __restrict__ group_size,
-    int32_t* __restrict__ union_count) {
+    int32_t* __restrict__ union_count, int halves) {
   __shared__ uint32_t rows[64][33];                    // +1 dword per row against bank conflicts
   // per-candidate partial scores of the (up to 8) waves, wave-major so that the writes
   // and the reads (stride 64 dwords) are free of bank conflicts; two buffers, alternating
   // per pick, so one barrier per pick suffices
   __shared__ int part[2][kFusedMaxWaves][64];
-  __shared__ int usz_acc[64];   // union size of each of the window's (<= 64) groups
+  __shared__ int usz_acc[128];  // union size of each of the window's (<= 64) groups or halves
   const int g = blockIdx.y;
   const int start = blockIdx.x * window;
   const int len = min(window, nq - start);
@@ -356,7 +360,8 @@ __global__ __launch_bounds__(64 * kFusedMaxWaves) void k_prepare(
   int pb = 0;   // partial-score buffer of the next pick
   if (nwaves > 1)
     for (int i = tid; i < 2 * 64 * kFusedMaxWaves; i += blockDim.x) (&part[0][0][0])[i] = 0;
-  for (int i = tid; i < 64; i += blockDim.x) usz_acc[i] = 0;
+  for (int i = tid; i < 128; i += blockDim.x) usz_acc[i] = 0;
+  const int half_w = halves ? max_group / 2 : max_group;   // members in the first half
   __syncthreads();
   while (free_mask) {
     const int seed = __builtin_ctzll(free_mask);
@@ -367,10 +372,20 @@ __global__ __launch_bounds__(64 * kFusedMaxWaves) void k_prepare(
       ulo[i] = __builtin_amdgcn_readlane(lo[i], seed);
       uhi[i] = __builtin_amdgcn_readlane(hi[i], seed);
     }
+    // halves: the first half's union (U until the half is complete) and the second's
+    uint32_t h0lo[kFusedWordsPerWave] = {}, h0hi[kFusedWordsPerWave] = {};
+    uint32_t h1lo[kFusedWordsPerWave] = {}, h1hi[kFusedWordsPerWave] = {};
     int members[8];
     members[0] = seed;
     int cnt = 1;
     while (cnt < max_group && free_mask) {
+      if (cnt == half_w) {   // (uniform) the first half is complete
+#pragma unroll
+        for (int i = 0; i < kFusedWordsPerWave; ++i) {
+          h0lo[i] = ulo[i];
+          h0hi[i] = uhi[i];
+        }
+      }
       int partial = 0;
 #pragma unroll
       for (int i = 0; i < kFusedWordsPerWave; ++i)
@@ -393,19 +408,45 @@ __global__ __launch_bounds__(64 * kFusedMaxWaves) void k_prepare(
       free_mask &= ~(1ull << pick);
 #pragma unroll
       for (int i = 0; i < kFusedWordsPerWave; ++i) {
-        ulo[i] |= __builtin_amdgcn_readlane(lo[i], pick);
-        uhi[i] |= __builtin_amdgcn_readlane(hi[i], pick);
+        const uint32_t plo = __builtin_amdgcn_readlane(lo[i], pick);
+        const uint32_t phi = __builtin_amdgcn_readlane(hi[i], pick);
+        ulo[i] |= plo;
+        uhi[i] |= phi;
+        if (cnt >= half_w) {   // (uniform) a member of the second half
+          h1lo[i] |= plo;
+          h1hi[i] |= phi;
+        }
       }
 #pragma unroll
       for (int j = 1; j < 8; ++j) if (j == cnt) members[j] = pick;
       ++cnt;
     }
-    // union size: popcount of U over every wave's words, summed by LDS atomics (read
-    // after the loop, so no barrier per group)
-    int usz = 0;
+    // union sizes: popcount over every wave's words, summed by LDS atomics (read after the
+    // loop, so no barrier per group)
+    if (halves) {
+      if (cnt <= half_w) {   // (uniform) no second half: the first half's union is U
 #pragma unroll
-    for (int i = 0; i < kFusedWordsPerWave; ++i) usz += __builtin_popcount(ulo[i]) + __builtin_popcount(uhi[i]);
-    if (lane == 0) atomicAdd(&usz_acc[gi], usz);
+        for (int i = 0; i < kFusedWordsPerWave; ++i) {
+          h0lo[i] = ulo[i];
+          h0hi[i] = uhi[i];
+        }
+      }
+      int s0 = 0, s1 = 0;
+#pragma unroll
+      for (int i = 0; i < kFusedWordsPerWave; ++i) {
+        s0 += __builtin_popcount(h0lo[i]) + __builtin_popcount(h0hi[i]);
+        s1 += __builtin_popcount(h1lo[i]) + __builtin_popcount(h1hi[i]);
+      }
+      if (lane == 0) {
+        atomicAdd(&usz_acc[2 * gi], s0);
+        atomicAdd(&usz_acc[2 * gi + 1], s1);
+      }
+    } else {
+      int usz = 0;
+#pragma unroll
+      for (int i = 0; i < kFusedWordsPerWave; ++i) usz += __builtin_popcount(ulo[i]) + __builtin_popcount(uhi[i]);
+      if (lane == 0) atomicAdd(&usz_acc[gi], usz);
+    }
     if (wave == 0) {
       if (lane < max_group) {
         int v = -1;
@@ -418,7 +459,11 @@ __global__ __launch_bounds__(64 * kFusedMaxWaves) void k_prepare(
     ++gi;
   }
   __syncthreads();   // (every wave made the same picks, so all arrive here)
-  if (tid < gi) union_count[gbase + tid + 1] = usz_acc[tid];
+  if (halves) {
+    if (tid < 2 * gi) union_count[2 * gbase + tid + 1] = usz_acc[tid];
+  } else if (tid < gi) {
+    union_count[gbase + tid + 1] = usz_acc[tid];
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -868,14 +913,21 @@ pw_status launch_prepare(const int32_t* topk, int nq, int hkv, int k, int n_page
                          int max_group, int n_groups, uint64_t* bits, int32_t* bad_id_count,
                          int32_t* group_qids, int32_t* group_size, int32_t* union_off,
                          int32_t* union_pages, uint8_t* union_qmask, int64_t capacity,
-                         int32_t* item_order, hipStream_t stream) {
+                         int32_t* item_order, int halves, hipStream_t stream) {
   const int words = (n_pages + 63) / 64;
-  const int n_tables = hkv * n_groups;
+  // halves: table 2j + h is half h of group j, members [h mg/2, (h + 1) mg/2) of its list,
+  // read through the member lists viewed as [hkv][2 n_groups][mg/2] (absent members are -1)
+  const int n_tables = hkv * n_groups * (halves ? 2 : 1);
+  const int32_t* t_rows = group_qids;
+  const int32_t* t_size = halves ? nullptr : group_size;
+  const int t_groups = halves ? 2 * n_groups : n_groups;
+  const int t_width = halves ? max_group / 2 : max_group;
   if (nq > 0) {
     const int nwaves = (words + kFusedWordsPerWave - 1) / kFusedWordsPerWave;
     dim3 grid((nq + window - 1) / window, hkv), block(nwaves * kWave);
     hipLaunchKernelGGL(k_prepare, grid, block, 0, stream, topk, nq, hkv, k, n_pages, words, window,
-                       max_group, n_groups, bits, bad_id_count, group_qids, group_size, union_off);
+                       max_group, n_groups, bits, bad_id_count, group_qids, group_size, union_off,
+                       halves);
     pw_status st = check_launch("prepare");
     if (st != PW_OK) return st;
   }
@@ -887,16 +939,16 @@ pw_status launch_prepare(const int32_t* topk, int nq, int hkv, int k, int n_page
     const int threads = schedule_threads(per);
     const int wpb = threads / kWave;
     hipLaunchKernelGGL(k_union_emit_schedule, dim3(8 + (n_tables + wpb - 1) / wpb), dim3(threads),
-                       schedule_lds_bytes(per), stream, bits, nq, words, group_qids, group_size,
-                       n_groups, n_tables, max_group, union_off, union_pages, union_qmask, capacity,
-                       per, item_order);
+                       schedule_lds_bytes(per), stream, bits, nq, words, t_rows, t_size, t_groups,
+                       n_tables, t_width, union_off, union_pages, union_qmask, capacity, per,
+                       item_order);
     return check_launch("union_emit_schedule");
   }
   const int wpb = 4;
   const int blocks = (n_tables + wpb - 1) / wpb;
   hipLaunchKernelGGL(k_union_emit<true>, dim3(blocks), dim3(wpb * kWave), 0, stream, bits, nq,
-                     words, group_qids, group_size, n_groups, n_tables, max_group, union_off,
-                     union_pages, union_qmask, capacity);
+                     words, t_rows, t_size, t_groups, n_tables, t_width, union_off, union_pages,
+                     union_qmask, capacity);
   return check_launch("union_emit");
 }
 

@@ -157,6 +157,18 @@ def test_prepare_validation(args, code):
     assert st == code and msg.startswith("pw_prepare"), msg
 
 
+@pytest.mark.parametrize("args,code", [
+    # as pw_prepare; the halves' 16 tables of width 4 need 16 * min(16, 4 * 4) = 256 entries
+    ((NULL, 64, 1, 4, 16, 64, 7, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 512, NULL, NULL), -1),  # odd mg
+    ((NULL, 64, 1, 4, 16, 64, 10, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 512, NULL, NULL), -2),  # mg 10
+    ((NULL, 64, 1, 4, 16, 64, 8, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 255, NULL, NULL), -3),  # capacity
+    ((NULL, 64, 1, 4, 16, 64, 8, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 256, NULL, NULL), -1),  # nulls
+])
+def test_prepare_halves_validation(args, code):
+    st, msg = _err(L.pw_prepare_halves(*args))
+    assert st == code and msg.startswith("pw_prepare_halves"), msg
+
+
 def _append(**kw):
     a = dict(k_new=NULL, v_new=NULL, n_tok=10, hkv=2, d=128, stride_tok=256, first=0, kc=NULL,
              vc=NULL, kv_dtype=0, ks=NULL, vs=NULL, ps=64, n_pages=4, sh=4 * 64 * 128,

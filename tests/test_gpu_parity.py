@@ -225,6 +225,60 @@ def test_half_groups_bit_identical(kw):
     check_lse(res[1][1].numpy(), L, "halves")
 
 
+HALF_PREP_SHAPES = [
+    dict(hq=8, hkv=2, nq=200, k=16, kv_len=8192, kv_dtype="fp8", window=64, max_group=8),
+    dict(hq=4, hkv=1, nq=77, k=8, kv_len=4096, window=16, max_group=4),       # ragged last window
+    dict(hq=2, hkv=1, nq=130, k=6, kv_len=8192, window=60, max_group=6),      # odd half width 3
+    dict(hq=2, hkv=2, nq=90, k=5, kv_len=4096, window=64, max_group=2),       # halves of one member
+    dict(hq=4, hkv=1, nq=100, k=8, kv_len=70016, window=64, max_group=8),     # 1094 pages: separate steps
+    dict(hq=4, hkv=1, nq=150, k=8, kv_len=8192, window=128, max_group=8),     # W = 128: separate steps
+]
+
+
+@pytest.mark.parametrize("kw", HALF_PREP_SHAPES,
+                         ids=["mg8", "mg4-ragged", "mg6", "mg2", "pages1094", "w128"])
+def test_fused_half_tables_equal_separate_steps(kw):
+    """pw_prepare_halves (bitsets, groups, the halves' union tables and their work order in
+    the fused launches where the shape allows) writes the bytes of the separate calls -
+    pw_page_bitsets, pw_group, pw_union_tables over the member lists viewed as halves,
+    pw_schedule_items - and the tables are the oracle's unions of each half."""
+    from gpu_util import make_plan
+    cfg = _small(**kw)
+    print(f"[parity] fused half tables {kw}", flush=True)
+    w = make_workload(cfg)
+    w.topk = add_padding_and_duplicates(w.topk, seed=cfg.seed + 5)
+    d = device_inputs(w)
+    plans = []
+    for fused in (True, False):
+        base = make_plan(w)
+        plan = type(base)(**{**{f: getattr(base, f) for f in ("nq", "hq", "hkv", "d", "n_pages", "page_size",
+                                                               "kv_len", "k", "window", "max_group", "mode",
+                                                               "grouping", "n_rows")},
+                             "fused": fused, "halves": True})
+        for t in (plan.union_off, plan.union_pages, plan.group_qids, plan.item_order):
+            t.fill_(-7)
+        plan.union_qmask.fill_(0xAB)
+        plan.prepare(d["ids"])
+        plans.append(plan)
+    torch.cuda.synchronize()
+    a, b = plans
+    total = int(a.union_off[-1].item())
+    assert torch.equal(a.bits, b.bits)
+    assert torch.equal(a.group_qids, b.group_qids) and torch.equal(a.group_size, b.group_size)
+    assert torch.equal(a.union_off, b.union_off)
+    assert torch.equal(a.union_pages[:total], b.union_pages[:total])
+    assert torch.equal(a.union_qmask[:total], b.union_qmask[:total])
+    assert torch.equal(a.item_order, b.item_order)
+    ref = oracle_tables(w)
+    bits = prep.page_bitsets(w.topk, cfg.n_pages)
+    h = cfg.max_group // 2
+    halves_per_head = [[x for m in grp for x in (m[:h], m[h:])] for grp in ref["groups"]]
+    off, pages, qmask = prep.union_tables(bits, halves_per_head)
+    assert np.array_equal(a.union_off.cpu().numpy(), off)
+    assert np.array_equal(a.union_pages[:total].cpu().numpy(), pages)
+    assert np.array_equal(a.union_qmask[:total].cpu().numpy(), qmask)
+
+
 @pytest.mark.parametrize("n_split", [1, 2, 3, 7])
 def test_block_union_table_slices(n_split):
     """Shared per-KV-group tables cut into n_split slices (partials merged by lse) give the
