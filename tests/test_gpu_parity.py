@@ -235,9 +235,10 @@ HALF_PREP_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("schedule", [True, False], ids=["order", "no-order"])
 @pytest.mark.parametrize("kw", HALF_PREP_SHAPES,
                          ids=["mg8", "mg4-ragged", "mg6", "mg2", "pages1094", "w128"])
-def test_fused_half_tables_equal_separate_steps(kw):
+def test_fused_half_tables_equal_separate_steps(kw, schedule):
     """pw_prepare_halves (bitsets, groups, the halves' union tables and their work order in
     the fused launches where the shape allows) writes the bytes of the separate calls -
     pw_page_bitsets, pw_group, pw_union_tables over the member lists viewed as halves,
@@ -254,9 +255,10 @@ def test_fused_half_tables_equal_separate_steps(kw):
         plan = type(base)(**{**{f: getattr(base, f) for f in ("nq", "hq", "hkv", "d", "n_pages", "page_size",
                                                                "kv_len", "k", "window", "max_group", "mode",
                                                                "grouping", "n_rows")},
-                             "fused": fused, "halves": True})
+                             "fused": fused, "halves": True, "schedule": schedule})
         for t in (plan.union_off, plan.union_pages, plan.group_qids, plan.item_order):
-            t.fill_(-7)
+            if t is not None:
+                t.fill_(-7)
         plan.union_qmask.fill_(0xAB)
         plan.prepare(d["ids"])
         plans.append(plan)
@@ -268,7 +270,9 @@ def test_fused_half_tables_equal_separate_steps(kw):
     assert torch.equal(a.union_off, b.union_off)
     assert torch.equal(a.union_pages[:total], b.union_pages[:total])
     assert torch.equal(a.union_qmask[:total], b.union_qmask[:total])
-    assert torch.equal(a.item_order, b.item_order)
+    assert (a.item_order is None) == (not schedule)
+    if schedule:
+        assert torch.equal(a.item_order, b.item_order)
     ref = oracle_tables(w)
     bits = prep.page_bitsets(w.topk, cfg.n_pages)
     h = cfg.max_group // 2
