@@ -71,8 +71,24 @@ def test_chunked_prefill_matches_oracle_and_serial(kv_dtype):
     ser = _run(chunks, n_pages, kv_dtype, overlap=False)
     for a, b in zip(got, ser):
         assert np.array_equal(a, b)
+    _check_against_oracle(chunks, got, n_pages, kv_dtype)
+
+
+def test_chunked_prefill_wide_groups_as_halves():
+    """Eight query heads per KV head make 64-row groups, which every chunk's plan runs as
+    two halves (the fused half-table preparation on the side stream): overlap equals
+    serial bit for bit, and every row matches the oracle."""
+    bounds = [0, 700, 1500, 2200]
+    chunks, n_pages = _make_chunks("fp8", bounds, hq=16, seed=3)
+    got = _run(chunks, n_pages, "fp8", overlap=True, hq=16)
+    ser = _run(chunks, n_pages, "fp8", overlap=False, hq=16)
+    for a, b in zip(got, ser):
+        assert np.array_equal(a, b)
+    _check_against_oracle(chunks, got, n_pages, "fp8")
+
+
+def _check_against_oracle(chunks, got, n_pages, kv_dtype, hkv=2, ps=64, d=128):
     # oracle: append chunk by chunk; attend each chunk on the cache as it stood then
-    hkv, ps, d = 2, 64, 128
     if kv_dtype == "fp8":
         k = np.zeros((hkv, n_pages, ps, d), np.uint8)
         ks = np.ones((hkv, n_pages), np.float32)
