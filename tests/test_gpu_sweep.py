@@ -3,8 +3,8 @@
 Each case draws head counts (G = 1, 2, 4, 8 query heads per KV head), d, the KV type,
 page size, context length, chunk size, TopK, grouping window and group size, optional
 padding / duplicate / out-of-range IDs and the half-group execution, then checks the
-groups, union tables and work order bit for bit and the attention output and lse within
-the tolerances."""
+groups, union tables (of the groups, or of their halves) and work order bit for bit and the
+attention output and lse within the tolerances."""
 import random
 
 import numpy as np
@@ -62,13 +62,18 @@ def test_random_shape(i, long):
     ref = oracle_tables(w)
     assert np.array_equal(plan.group_qids.cpu().numpy(), ref["group_qids"])
     assert np.array_equal(plan.group_size.cpu().numpy(), ref["group_size"])
-    if not halves:
-        n = int(plan.union_off[-1])
-        assert np.array_equal(plan.union_off.cpu().numpy(), ref["union_off"])
-        assert np.array_equal(plan.union_pages[:n].cpu().numpy(), ref["union_pages"])
-        assert np.array_equal(plan.union_qmask[:n].cpu().numpy(), ref["union_qmask"])
-        sizes = np.diff(ref["union_off"].astype(np.int64))
-        assert np.array_equal(plan.item_order.cpu().numpy(), np.array(prep.work_order(sizes.tolist())))
+    if halves:   # the tables of each group's two member halves, in pick order
+        h = cfg.max_group // 2
+        halves_per_head = [[x for m in grp for x in (m[:h], m[h:])] for grp in ref["groups"]]
+        r_off, r_pages, r_qmask = prep.union_tables(prep.page_bitsets(w.topk, cfg.n_pages), halves_per_head)
+    else:
+        r_off, r_pages, r_qmask = ref["union_off"], ref["union_pages"], ref["union_qmask"]
+    n = int(plan.union_off[-1])
+    assert np.array_equal(plan.union_off.cpu().numpy(), r_off)
+    assert np.array_equal(plan.union_pages[:n].cpu().numpy(), r_pages)
+    assert np.array_equal(plan.union_qmask[:n].cpu().numpy(), r_qmask)
+    sizes = np.diff(np.asarray(r_off, dtype=np.int64))
+    assert np.array_equal(plan.item_order.cpu().numpy(), np.array(prep.work_order(sizes.tolist())))
     O, L = oracle_attention(w, ref["S"])
     check_close(out.float().cpu().numpy(), O, cfg.kv_dtype, f"case {i}")
     check_lse(lse.cpu().numpy(), L, f"case {i}")
