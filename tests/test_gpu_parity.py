@@ -97,6 +97,30 @@ def test_small_shapes(kw):
     check_lse(res["lse"], L, str(kw))
 
 
+MAX_SHAPES = [
+    # the preparation's page limit (4096 pages: the separate steps) with TopK 512 per query
+    dict(hq=2, hkv=1, d=64, ps=64, kv_len=262144, nq=16, k=512, window=16, max_group=8, kv_dtype="fp8"),
+    # the largest grouping window (1024 candidates: the general grouping kernel)
+    dict(hq=1, hkv=1, d=64, ps=64, kv_len=70400, nq=1024, k=64, window=1024, max_group=8, kv_dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("kw", MAX_SHAPES, ids=["pages4096-k512", "window1024"])
+def test_maximum_sizes(kw):
+    """The limits of the preparation calls (4096 pages, TopK 512, a 1024-query window) through
+    the whole path: tables bit-exact, every output row and lse within tolerance."""
+    cfg = Config(name="max", support="uniform", forced=True, seed=77, **kw)
+    print(f"[parity] maximum sizes {kw}", flush=True)
+    w = make_workload(cfg)
+    res, _ = run_gpu(w)
+    ref = oracle_tables(w)
+    _compare_tables(res, ref)
+    assert res["bad_ids"] == 0
+    O, L = oracle_attention(w, ref["S"])
+    check_close(res["out"], O, cfg.kv_dtype, "maximum sizes")
+    check_lse(res["lse"], L, "maximum sizes")
+
+
 def test_future_pages_and_empty_supports():
     cfg = _small(nq=200, kv_len=1024, k=3, hq=8, hkv=2)   # queries on pages 12..15
     w = make_workload(cfg)
