@@ -206,10 +206,13 @@ struct Cfg {
   // Waves per SIMD the tile ring's LDS admits (160 KiB per CU, 4 SIMDs).  Where it admits
   // three, the kernel is built for three (<= 168 VGPRs) and streams its K fragments
   // instead of holding a whole tile's; elsewhere two waves with the K tile held in
-  // registers are faster.
+  // registers are faster.  One-row-tile items whose ring admits ten waves per CU (two
+  // SIMDs can then hold three) are still held, but built for three waves (the 2K-query
+  // GQA bf16 chunk: attention -2 %, a few registers spilled outside the tile loop).
   static constexpr int kLdsWaves = (160 * 1024 / (ST * kStageBytes)) * NW / 4;
-  static constexpr int kWavesPerSimd = kLdsWaves >= 3 ? 3 : 2;
-  static constexpr bool kStreamK = kWavesPerSimd == 3;
+  static constexpr bool kStreamK = kLdsWaves >= 3;
+  static constexpr int kWavesPerSimd =
+      kStreamK || (MT == 1 && (160 * 1024 / (ST * kStageBytes)) * NW >= 10) ? 3 : 2;
   // fp8 K with d = 128: S^T = K . Q^T on the fp8 MFMA (16x16x128), K straight from LDS
   static constexpr bool kF8Mma = FP8 && D == 128;
 };
@@ -528,13 +531,16 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
 
   // ---- running state ------------------------------------------------------------------
   f32x4 o[MT][C::kDt];
-  float m_ref[MT], l_run[MT], thr[MT];   // thr: rescale threshold of the row-sum share (below)
+  // m_ref: the row's reference, +inf while it has none (so that log2 vs - m_ref is -inf and
+  // every P of the row is 0 until the reference is set); thr: rescale threshold of the
+  // row-sum share (below)
+  float m_ref[MT], l_run[MT], thr[MT];
   int mt_min[MT];   // smallest usable last token over the valid rows of a row tile
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
 #pragma unroll
     for (int dt = 0; dt < C::kDt; ++dt) o[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_ref[m] = -INFINITY;
+    m_ref[m] = INFINITY;
     l_run[m] = 0.f;
     thr[m] = -INFINITY;
     int lim = my_bit[m] != 0 ? row_lim[m] : 0x7fffffff;   // my_bit != 0: the row has a query
@@ -583,22 +589,22 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     c.pg = (pq & 0xFFFFFF) - 1;
     PW_DCHECK(lane != 0 || (c.pg >= 0 && l >= 0 && l < kWave));   // a listed page, held by the lanes
     c.qm = (int)((uint32_t)pq >> 24);
-    c.abits = 0;
+    // (adds and shifts only: x != 0 as (x + 2^n - 1) >> n for x < 2^n, which the compiler
+    // does not turn into compares, so that the mask stays in a scalar register)
+    int ab = 0;
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-      if (c.pg >= 0 && (c.qm & mt_members[m]) != 0) c.abits |= 1 << m;
+    for (int m = 0; m < MT; ++m) ab |= (int)(((uint32_t)(c.qm & mt_members[m]) + 0xFFu) >> 8) << m;
+    c.abits = ab & -(int)((((uint32_t)pq & 0xFFFFFFu) + 0xFFFFFFu) >> 24);   // (none for an invalid page)
     c.sc = lane_f(md_sc, l);
     c.lvs = lane_f(md_lvs, l);
     c.inv_vs = lane_f(md_ivs, l);
+    // (the values of a row tile that does not select the page are never read)
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      c.scm[m] = 0.f;
-      c.bias[m] = -INFINITY;
-      c.selm[m] = 0;
       if ((c.abits >> m) & 1) {   // uniform
         const bool sel = (c.qm & my_bit[m]) != 0;
         c.scm[m] = C::kF8Mma ? c.sc * qs[m] : c.sc;   // fp8 MFMA: undo the row's 2^e
-        c.bias[m] = sel && m_ref[m] != -INFINITY ? c.lvs - m_ref[m] : -INFINITY;
+        c.bias[m] = sel ? c.lvs - m_ref[m] : -INFINITY;   // (-inf too while m_ref = +inf)
         c.selm[m] = __builtin_amdgcn_ballot_w64(sel);
       }
     }
@@ -609,14 +615,29 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     constexpr int SS = decltype(stage_c)::value;
     const int pg = pc.pg, qm = pc.qm;
     const int tok0 = pg * p.page_size + (t & ((1 << tpp_shift) - 1)) * kTK;
-    bool act[MT];
-    bool any = false;
+    // bit m: row tile m selects the page and reaches into the tile.  Uniform; in the held
+    // forms built with integer operations only (tok0 <= mt_lim iff the sign bit of
+    // mt_lim - tok0 is clear; both are token indices below 2^30), so that it stays in a
+    // scalar register (compares leave it in a lane mask that is copied through a vector
+    // register; the streamed forms, at their register limit, spill less with compares)
+    int act_bits = 0;
+    bool act_b[MT];
+    if constexpr (C::kStreamK) {
+      bool any = false;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      act[m] = ((pc.abits >> m) & 1) != 0 && tok0 <= mt_lim[m];
-      any |= act[m];
+      for (int m = 0; m < MT; ++m) {
+        act_b[m] = ((pc.abits >> m) & 1) != 0 && tok0 <= mt_lim[m];
+        any |= act_b[m];
+      }
+      if (!any) return;
+    } else {
+      int reach = 0;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) reach |= (int)((~(uint32_t)(mt_lim[m] - tok0)) >> 31) << m;
+      act_bits = pc.abits & reach;
+      if (act_bits == 0) return;
     }
-    if (!any) return;
+    auto act = [&](int m) { return C::kStreamK ? act_b[m] : ((act_bits >> m) & 1) != 0; };
     const float sc = pc.sc;
     const float lvs = pc.lvs;
     const float inv_vs = pc.inv_vs;
@@ -678,8 +699,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       if constexpr (MT == 1) {
         qk_tiles(std::integral_constant<int, 1>{});
       } else {
-        if (act[0] && act[1]) qk_tiles(std::integral_constant<int, 3>{});
-        else if (act[0]) qk_tiles(std::integral_constant<int, 1>{});
+        if (act(0) && act(1)) qk_tiles(std::integral_constant<int, 3>{});
+        else if (act(0)) qk_tiles(std::integral_constant<int, 1>{});
         else qk_tiles(std::integral_constant<int, 2>{});
       }
     } else if constexpr (C::kF8Mma) {
@@ -706,17 +727,23 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
         return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
     };
+    // (held form: the reads are issued here and the fp8 codes converted right before the PV
+    // MFMAs, after one wait for every LDS read, instead of one wait per fragment)
     bf16x8 va[kEarlyV ? C::kDt : 1];
+    i32x2 va8[kEarlyV && FP8 ? C::kDt : 1];
     if constexpr (kEarlyV) {
 #pragma unroll
-      for (int dt = 0; dt < C::kDt; ++dt) va[dt] = vfrag(dt);
+      for (int dt = 0; dt < C::kDt; ++dt) {
+        if constexpr (FP8) va8[dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PW_LDS i32x2*)(st + v_off[dt]));
+        else va[dt] = vfrag(dt);
+      }
     }
 
     bf16x8 pf[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      pf[m] = bf16x8{};
-      if (!act[m]) continue;
+      if constexpr (!kEarlyV) pf[m] = bf16x8{};   // (this form's PV runs every row tile)
+      if (!act(m)) continue;
       f32x4 s2[2];
       if constexpr (C::kF8Mma && !C::kStreamK) {   // both key blocks' hi products, then lo
 #pragma unroll
@@ -749,9 +776,9 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       const bool tile_full = tok0 + kTK - 1 <= mt_min[m];          // uniform
       // scores in the log2 domain; keys after a row's last usable token -> -inf.  A tile
       // wholly before every row's limit (the common case) needs no causal compare.
-      auto scores = [&](float bias, float* x, auto masked_c) {
+      auto scores = [&](float bias, float* x, auto masked_c, int lim) {
         // key tok0 + 8lq + 4kb + ii is past the row's limit iff 4kb + ii > rel
-        const int rel = decltype(masked_c)::value ? row_lim[m] - tok0 - 8 * lq : 0;
+        const int rel = decltype(masked_c)::value ? lim - tok0 - 8 * lq : 0;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -766,9 +793,9 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       float pv[8];
       const float bias0 = pc.bias[m];
       if (tile_full)
-        scores(bias0, pv, std::false_type{});
+        scores(bias0, pv, std::false_type{}, 0);
       else
-        scores(bias0, pv, std::true_type{});
+        scores(bias0, pv, std::true_type{}, row_lim[m]);
       // P is rounded to bf16 for the PV MFMA, and the row sum adds up exactly those rounded
       // values: numerator and denominator then carry the same weights, so a row whose
       // softmax is dominated by one key gets that key's value without the rounding of its
@@ -802,20 +829,26 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
         const uint32_t rows = (uint32_t)(nb | (nb >> 16) | (nb >> 32) | (nb >> 48)) & 0xFFFFu;
         const bool need = (rows >> li) & 1u;
         float raw[8];
-        scores(sel ? 0.f : -INFINITY, raw, std::true_type{});
+        // (its own copy of the limit, so that the compiler does not share these compares
+        // with the fast path's and hoist them out of its masked branch)
+        int lim = row_lim[m];
+        asm volatile("" : "+v"(lim));
+        scores(sel ? 0.f : -INFINITY, raw, std::true_type{}, lim);
         float mloc = -INFINITY;
 #pragma unroll
         for (int k = 0; k < 8; ++k) mloc = fmaxf(mloc, raw[k]);
         mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-        const float m_new = need ? fmaxf(mloc, m_ref[m]) : m_ref[m];
-        const float alpha = m_ref[m] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref[m] - m_new);
+        const bool has_ref = m_ref[m] != INFINITY;
+        float m_new = need ? (has_ref ? fmaxf(mloc, m_ref[m]) : mloc) : m_ref[m];
+        if (m_new == -INFINITY) m_new = INFINITY;   // (no finite score: still no reference)
+        const float alpha = has_ref ? __builtin_amdgcn_exp2f(m_ref[m] - m_new) : 0.f;
         l_run[m] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < C::kDt; ++dt) o[m][dt] *= alpha;
         m_ref[m] = m_new;
-        thr[m] = m_new == -INFINITY ? -INFINITY : kRescaleShare;
-        pc.bias[m] = (sel && m_new != -INFINITY) ? lvs - m_new : -INFINITY;   // (the page's next tile)
+        thr[m] = m_new == INFINITY ? -INFINITY : kRescaleShare;
+        pc.bias[m] = sel ? lvs - m_new : -INFINITY;   // (the page's next tile)
         // only the rows that moved their reference recompute P: every other row keeps its
         // fast-path values, so a row's arithmetic never depends on its tile-mates
         if (need) {
@@ -831,10 +864,33 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     // MFMAs form one block behind one uniform branch, and an inactive row tile (P = 0)
     // skips its block; otherwise every row tile runs (its P is 0 when inactive).
     if constexpr (kEarlyV) {
+      // every fragment passes through one empty asm statement, so that the compiler waits
+      // once for all of them instead of before each conversion or MFMA
+      static_assert(C::kDt == 8 || C::kDt == 4, "d = 128 or 64");
+      if constexpr (FP8) {
+        if constexpr (C::kDt == 8)
+          asm volatile("" : "+v"(va8[0]), "+v"(va8[1]), "+v"(va8[2]), "+v"(va8[3]), "+v"(va8[4]), "+v"(va8[5]),
+                       "+v"(va8[6]), "+v"(va8[7]));
+        else
+          asm volatile("" : "+v"(va8[0]), "+v"(va8[1]), "+v"(va8[2]), "+v"(va8[3]));
+#pragma unroll
+        for (int dt = 0; dt < C::kDt; ++dt) va[dt] = fp8x8_to_bf16(va8[dt]);
+      } else {
+        i32x4 vr[C::kDt];
+#pragma unroll
+        for (int dt = 0; dt < C::kDt; ++dt) vr[dt] = __builtin_bit_cast(i32x4, va[dt]);
+        if constexpr (C::kDt == 8)
+          asm volatile("" : "+v"(vr[0]), "+v"(vr[1]), "+v"(vr[2]), "+v"(vr[3]), "+v"(vr[4]), "+v"(vr[5]),
+                       "+v"(vr[6]), "+v"(vr[7]));
+        else
+          asm volatile("" : "+v"(vr[0]), "+v"(vr[1]), "+v"(vr[2]), "+v"(vr[3]));
+#pragma unroll
+        for (int dt = 0; dt < C::kDt; ++dt) va[dt] = __builtin_bit_cast(bf16x8, vr[dt]);
+      }
       if constexpr (MT == 1) __builtin_amdgcn_s_setprio(1);   // (see the QK block above)
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        if (MT > 1 && !act[m]) continue;
+        if (MT > 1 && !act(m)) continue;
 #pragma unroll
         for (int dt = 0; dt < C::kDt; ++dt)
           o[m][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pf[m], o[m][dt], 0, 0, 0);
