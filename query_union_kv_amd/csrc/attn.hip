@@ -909,11 +909,13 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
 
   // ---- pipeline: tile t lives in stage t % ST; the loop is unrolled by ST so that every
   // stage offset is a compile-time immediate ------------------------------------------------
-  auto step = [&](int t, auto stage_c, PageCtx& pc, int pg_next) {
+  // (next_known: the caller knows that tile t + ST - 1 exists)
+  auto step = [&](int t, auto stage_c, PageCtx& pc, int pg_next, bool next_known = false) {
     constexpr int SS = decltype(stage_c)::value;
     wait_tiles<C::kDmaPerTile, ST - 2>(min(n_tiles - 1 - t, ST - 2));   // tile t has landed
     if constexpr (NW > 1) __builtin_amdgcn_s_barrier();                 // ... for every wave
-    if (t + ST - 1 < n_tiles) issue(t + ST - 1, std::integral_constant<int, (SS + ST - 1) % ST>{}, pg_next);
+    if (next_known || t + ST - 1 < n_tiles)
+      issue(t + ST - 1, std::integral_constant<int, (SS + ST - 1) % ST>{}, pg_next);
     compute(t, stage_c, pc);
   };
   // Several waves over a four-stage ring step by pairs of tiles: tiles t, t + 1 have landed
@@ -948,12 +950,12 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       if (t0 + 2 < n_tiles) pair(t0 + 2, S2{}, S3{}, S0{}, S1{});
     }
   } else if constexpr (ST == 2) {
-    // a page holds 2 or 4 tiles and t0 is even, so tiles t0 and t0 + 1 share a page: its
-    // values are read once, and the load of tile t0 + 1 needs no page lookup
+    // a page holds 2 or 4 tiles (n_tiles is even) and t0 is even, so tile t0 + 1 exists and
+    // shares t0's page: its values are read once, and its load needs no page lookup
     for (int t0 = 0; t0 < n_tiles; t0 += 2) {
       PageCtx pc = page_ctx(t0);   // (a rescale in tile t0 updates its bias for t0 + 1)
-      step(t0, std::integral_constant<int, 0>{}, pc, pc.pg);
-      if (t0 + 1 < n_tiles) step(t0 + 1, std::integral_constant<int, 1>{}, pc, kNoPage);
+      step(t0, std::integral_constant<int, 0>{}, pc, pc.pg, true);
+      step(t0 + 1, std::integral_constant<int, 1>{}, pc, kNoPage);
     }
   } else {
     for (int t0 = 0; t0 < n_tiles; t0 += ST) {
