@@ -499,14 +499,15 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
 
   // Every tile issues the same number of loads (an invalid page reads page 0 and is
   // never computed), so the vmcnt waits below are exact.
-  // pg_known: the tile's page when the caller has it already (kNoPage: look it up)
-  constexpr int kNoPage = -2;
-  auto issue = [&](int t, auto stage_c, int pg_known) {
+  // off_known: the byte offset of the tile's page when the caller has it already (from the
+  // load of the page's first tile; kNoPage: look it up).  Returns the page's byte offset.
+  constexpr int64_t kNoPage = -1;
+  auto issue = [&](int t, auto stage_c, int64_t off_known) -> int64_t {
     constexpr int SS = decltype(stage_c)::value;
     const int ent = t >> tpp_shift;
     int64_t pg_off;
-    if (pg_known != kNoPage) {
-      pg_off = (int64_t)max(pg_known, 0) * p.stride_page_b;
+    if (off_known != kNoPage) {
+      pg_off = off_known;
     } else if (ent - md_base < kWave) {   // held by the lanes (the loop never looks back)
       const int pg = (lane_i(md_pq, ent - md_base) & 0xFFFFFF) - 1;
       pg_off = (int64_t)__builtin_amdgcn_readfirstlane(max(pg, 0)) * p.stride_page_b;
@@ -527,6 +528,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     for (int i = 0; i < C::kDmaPerTensor; i += GN)
       dma16_group<GN, NW * 1024>(dma_off + i, vt,
                                  lds_base + SS * C::kStageBytes + C::kTensorBytes + (i * NW + wave) * (kWave * 16));
+    return pg_off;
   };
 
   // ---- running state ------------------------------------------------------------------
@@ -572,6 +574,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
   // what a tile needs of its page: shared by the tiles of one page
   struct PageCtx {
     int pg, qm, abits;        // page (-1: invalid), member mask, bit m: row tile m selects it
+    int tok_base;             // the page's first token
     float sc, lvs, inv_vs;    // score scale * ks, log2 vs, 1 / vs
     // per selecting row tile m (bit m of abits): the row's score scale, the bias of the
     // fast-path exponent (log2 vs - reference, or -inf for a row that did not select the page
@@ -587,6 +590,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     const int pq = lane_i(md_pq, l);
     PageCtx c;
     c.pg = (pq & 0xFFFFFF) - 1;
+    c.tok_base = c.pg * p.page_size;
     PW_DCHECK(lane != 0 || (c.pg >= 0 && l >= 0 && l < kWave));   // a listed page, held by the lanes
     c.qm = (int)((uint32_t)pq >> 24);
     // (adds and shifts only: x != 0 as (x + 2^n - 1) >> n for x < 2^n, which the compiler
@@ -613,8 +617,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
 
   auto compute = [&](int t, auto stage_c, PageCtx& pc) {
     constexpr int SS = decltype(stage_c)::value;
-    const int pg = pc.pg, qm = pc.qm;
-    const int tok0 = pg * p.page_size + (t & ((1 << tpp_shift) - 1)) * kTK;
+    const int qm = pc.qm;
+    const int tok0 = pc.tok_base + (t & ((1 << tpp_shift) - 1)) * kTK;
     // bit m: row tile m selects the page and reaches into the tile.  Uniform; in the held
     // forms built with integer operations only (tok0 <= mt_lim iff the sign bit of
     // mt_lim - tok0 is clear; both are token indices below 2^30), so that it stays in a
@@ -792,10 +796,15 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       // fast path: P = exp2(s*sc - reference + log2 vs) with the current reference
       float pv[8];
       const float bias0 = pc.bias[m];
-      if (tile_full)
+      // the lanes whose row reaches into the tile (all in a full tile; tile_full is tested
+      // once, so the compiler keeps it a scalar compare rather than a lane mask)
+      uint64_t reach_rows = ~uint64_t(0);
+      if (tile_full) {
         scores(bias0, pv, std::false_type{}, 0);
-      else
+      } else {
         scores(bias0, pv, std::true_type{}, row_lim[m]);
+        reach_rows = __builtin_amdgcn_ballot_w64(tok0 <= row_lim[m]);
+      }
       // P is rounded to bf16 for the PV MFMA, and the row sum adds up exactly those rounded
       // values: numerator and denominator then carry the same weights, so a row whose
       // softmax is dominated by one key gets that key's value without the rounding of its
@@ -822,8 +831,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       // A lane needs it when its row selected the page and reaches into the tile, and its
       // share of the row sum is above thr (-inf while the row has no reference, else 2^30;
       // the row sum is never negative, so this is "no reference yet, or above 2^30").
-      uint64_t nb = __builtin_amdgcn_ballot_w64(!(lsum * inv_vs <= thr[m])) & pc.selm[m];
-      if (!tile_full) nb &= __builtin_amdgcn_ballot_w64(tok0 <= row_lim[m]);
+      const uint64_t nb = __builtin_amdgcn_ballot_w64(!(lsum * inv_vs <= thr[m])) & pc.selm[m] & reach_rows;
       if (nb) {
         const bool sel = (qm & my_bit[m]) != 0;
         const uint32_t rows = (uint32_t)(nb | (nb >> 16) | (nb >> 32) | (nb >> 48)) & 0xFFFFu;
@@ -909,14 +917,17 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
 
   // ---- pipeline: tile t lives in stage t % ST; the loop is unrolled by ST so that every
   // stage offset is a compile-time immediate ------------------------------------------------
-  // (next_known: the caller knows that tile t + ST - 1 exists)
-  auto step = [&](int t, auto stage_c, PageCtx& pc, int pg_next, bool next_known = false) {
+  // (next_known: the caller knows that tile t + ST - 1 exists; off_next: its page's byte
+  // offset, or kNoPage; returns the page offset of the load issued, kNoPage if none)
+  auto step = [&](int t, auto stage_c, PageCtx& pc, int64_t off_next, bool next_known = false) {
     constexpr int SS = decltype(stage_c)::value;
     wait_tiles<C::kDmaPerTile, ST - 2>(min(n_tiles - 1 - t, ST - 2));   // tile t has landed
     if constexpr (NW > 1) __builtin_amdgcn_s_barrier();                 // ... for every wave
+    int64_t off = kNoPage;
     if (next_known || t + ST - 1 < n_tiles)
-      issue(t + ST - 1, std::integral_constant<int, (SS + ST - 1) % ST>{}, pg_next);
+      off = issue(t + ST - 1, std::integral_constant<int, (SS + ST - 1) % ST>{}, off_next);
     compute(t, stage_c, pc);
+    return off;
   };
   // Several waves over a four-stage ring step by pairs of tiles: tiles t, t + 1 have landed
   // for every wave and every wave is done with t - 2, t - 1, whose stages then take t + 2 and
@@ -937,7 +948,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
       compute(t + 1, sb, c);
     }
   };
-  if (0 < n_tiles) issue(0, std::integral_constant<int, 0>{}, kNoPage);
+  int64_t page_off = kNoPage;   // (two-stage ring) byte offset of the next pair's page
+  if (0 < n_tiles) page_off = issue(0, std::integral_constant<int, 0>{}, kNoPage);
   if constexpr (ST > 2) if (1 < n_tiles) issue(1, std::integral_constant<int, 1>{}, kNoPage);
   if constexpr (ST > 3 && !kPairs) if (2 < n_tiles) issue(2, std::integral_constant<int, 2>{}, kNoPage);
   if constexpr (kPairs) {
@@ -954,8 +966,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(Cfg<
     // shares t0's page: its values are read once, and its load needs no page lookup
     for (int t0 = 0; t0 < n_tiles; t0 += 2) {
       PageCtx pc = page_ctx(t0);   // (a rescale in tile t0 updates its bias for t0 + 1)
-      step(t0, std::integral_constant<int, 0>{}, pc, pc.pg, true);
-      step(t0 + 1, std::integral_constant<int, 1>{}, pc, kNoPage);
+      step(t0, std::integral_constant<int, 0>{}, pc, page_off, true);
+      page_off = step(t0 + 1, std::integral_constant<int, 1>{}, pc, kNoPage);
     }
   } else {
     for (int t0 = 0; t0 < n_tiles; t0 += ST) {
