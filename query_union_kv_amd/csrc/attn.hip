@@ -128,23 +128,24 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 v) {
 // address; declared clobbered, so the compiler restores whatever it keeps there).  Load k
 // reads sbase + voff[k] + k*STRIDE (sbase wave-uniform, voff per lane) and lands at LDS
 // m0 + k*STRIDE + 16*l for lane l: the instruction offset applies to both addresses
-// (measured).  The offset field holds < 4096.  The leading s_nop separates the M0 write
-// from a preceding load that reads M0.
+// (measured).  The offset field holds < 4096.  An s_nop gives the one wait state an M0
+// write needs before an LDS-DMA load reads it (the compiler keeps the same distance for
+// its own M0 writes; a load that reads M0 may be followed by an M0 write at once).
 template <int N, int STRIDE>
 __device__ __forceinline__ void dma16_group(const uint32_t* voff, const void* sbase, uint32_t m0) {
   static_assert((N == 1 || N == 2 || N == 4) && (N - 1) * STRIDE < 4096, "offset field");
   if constexpr (N == 1) {
     asm volatile(
-        "s_nop 0\n\t"
         "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
         "global_load_lds_dwordx4 %0, %2"
         :
         : "v"(voff[0]), "s"(m0), "s"(sbase)
         : "memory", "m0");
   } else if constexpr (N == 2) {
     asm volatile(
-        "s_nop 0\n\t"
         "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
         "global_load_lds_dwordx4 %0, %3\n\t"
         "global_load_lds_dwordx4 %1, %3 offset:%4"
         :
@@ -152,8 +153,8 @@ __device__ __forceinline__ void dma16_group(const uint32_t* voff, const void* sb
         : "memory", "m0");
   } else {
     asm volatile(
-        "s_nop 0\n\t"
         "s_mov_b32 m0, %4\n\t"
+        "s_nop 0\n\t"
         "global_load_lds_dwordx4 %0, %5\n\t"
         "global_load_lds_dwordx4 %1, %5 offset:%6\n\t"
         "global_load_lds_dwordx4 %2, %5 offset:%7\n\t"
